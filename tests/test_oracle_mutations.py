@@ -1,0 +1,59 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case copies oracle.c, plants one mistake by a text substitution, builds
+the copy on the CPU, and runs the fast oracle pin tests against it in a
+subprocess (ORACLE_LIB selects the library).  Every mutant must make at
+least one pin fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "ties_away_from_zero": ("nearbyint(a / q)", "round(a / q)"),
+    "no_saturation": ("a = F->maxval;                      /* saturation */", "(void)0;"),
+    "sign_dropped": ("return (uint8_t)(sign | (field_e << F->mbits) | field_m);",
+                     "return (uint8_t)((field_e << F->mbits) | field_m);"),
+    "e5m2_bias_16": ("{ 5, 2, 15, 57344.0 }", "{ 5, 2, 16, 57344.0 }"),
+    "fp8_subnormal_exponent": ("v = ldexp((double)m, 1 - F->bias - F->mbits);",
+                               "v = ldexp((double)m, -F->bias - F->mbits);"),
+    "f16_subnormal_exponent": ("v = ldexp((double)m, -14 - 10);", "v = ldexp((double)m, -15 - 10);"),
+    "unscale_divides": ("float y = orc_f16_to_f32(g[i]) * inv;", "float y = orc_f16_to_f32(g[i]) / S;"),
+    "check_inputs_not_outputs": ("if (!isfinite(y))\n                any = 1;",
+                                 "if (!isfinite(orc_f16_to_f32(g[i])))\n                any = 1;"),
+    "no_canonical_nan": ("o[i] = f32_of_bits(CANONICAL_NAN);", "o[i] = y;"),
+    "growth_strict_gt": ("if (*tracker >= interval)", "if (*tracker > interval)"),
+    "tracker_kept_on_skip": ("*tracker = 0;\n        if (skips)", "if (skips)"),
+    "flag_not_cleared": ("    *found_inf = 0;\n}", "}"),
+    "amax_counts_inf": ("if (isfinite(f) && fabsf(f) > amax)", "if (!isnan(f) && fabsf(f) > amax)"),
+    "no_floor": ("float a = amax > floor_ ? amax : floor_;", "float a = amax; (void)floor_;"),
+    "scale_inverted": ("return a / (float)fmt_max(fmt);", "return (float)fmt_max(fmt) / a;"),
+    "multiply_by_reciprocal": ("float y = f / s;", "float y = f * (1.0f / s);"),
+    "dequant_block_transposed": ("(r / br) * nbc + c / bc;", "(c / bc) * nbc + r / br;"),
+    "nan_input_unsigned": ("return (uint8_t)((signbit(f) ? 0x80 : 0x00) | 0x7F);", "return 0x7F;"),
+}
+
+FAST_PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_unscale.py",
+             "tests/test_oracle_quant.py"]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not unique/absent: %r" % old
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
+                    "-fPIC", "-shared", "-w", "-o", str(so), str(mut), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not slow and not gpu",
+                        "-p", "no:cacheprovider", *FAST_PINS],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "mutant %s survived every pin:\n%s" % (name, r.stdout[-2000:])
