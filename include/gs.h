@@ -1,0 +1,176 @@
+/*
+ * gs.h -- C ABI of libgsfp8: dynamic loss scaling and FP8 scaled casting on
+ * AMD MI355X (gfx950).
+ *
+ * Every entry point takes plain pointers and sizes.  Pointers documented as
+ * "device" are HIP device allocations on the current device; "host" pointers
+ * are read during the call only.  All work is enqueued on `stream` (a
+ * hipStream_t; NULL means the null stream), asynchronously: no call
+ * synchronises the host, reads device memory from the host, or allocates on
+ * a repeated call with the same arguments.  Device buffers must stay alive
+ * until the enqueued work has finished.
+ *
+ * Errors: argument errors are detected on the host and returned before
+ * anything is enqueued, with no side effects.  Non-finite DATA is never an
+ * error; it is reported through the found_inf / nonfinite flags.  A failing
+ * HIP call returns GS_ERR_HIP.
+ *
+ * Sources (cited by page title and section):
+ *   "Loss scaling, FP8, and the failure that never crashes" -- section
+ *     "Loss scaling, derived from the chain rule you already have" (scaled
+ *     loss S*L gives scaled gradients S*g; recovered gradient g_scaled / S in
+ *     FP32; skip and halve on Inf/NaN, double after a run of clean steps) and
+ *     the SimpleGradScaler listing of the worked-example section.
+ *   "Numerical Precision, Mixed Precision, and Loss Scaling" -- the FP8
+ *     specification paragraph (OCP E4M3 / E5M2), the FP16 range paragraph,
+ *     the GradScaler defaults paragraph (65536, x2.0, x0.5, 2000) and the
+ *     six-step AMP sequence (unscale and inspect; skip invalid steps;
+ *     adjust the scale).
+ *   "Why FP8 training is stable" -- "How it works", Failure 1 (one FP32 s:
+ *     store x/s, multiply by s on the way out; s from the current max-abs)
+ *     and "The seam" (1x128 activation tiles, 128x128 weight blocks).
+ *   "Mixed precision and FP8 training" -- section "FP8 training",
+ *     fp8_scaling.py (quant, per_tensor, per_block with the 1e-12 floor).
+ */
+#ifndef GS_FP8_H
+#define GS_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gs_status;
+#define GS_OK             0
+#define GS_ERR_NULL      -1  /* a required pointer is NULL                          */
+#define GS_ERR_SIZE      -2  /* negative count or size, or too large                */
+#define GS_ERR_SHAPE     -3  /* block granularity does not divide rows x cols        */
+#define GS_ERR_DTYPE     -4  /* unsupported element type for this call               */
+#define GS_ERR_ARG       -5  /* bad enum value, factor or interval                   */
+#define GS_ERR_ALIGN     -6  /* pointer not aligned to its element size              */
+#define GS_ERR_WORKSPACE -7  /* workspace missing or smaller than required           */
+#define GS_ERR_HIP       -8  /* a HIP runtime call or kernel launch failed           */
+
+typedef enum { GS_F16 = 1, GS_BF16 = 2, GS_F32 = 3 } gs_dtype;
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
+typedef enum { FP8_PER_TENSOR = 0, FP8_BLOCK_1x128 = 1, FP8_BLOCK_128x128 = 2 } fp8_granularity;
+typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
+
+/*
+ * gs_unscale_check -- fused multi-tensor unscale + non-finite check.
+ * "Loss scaling, FP8, and the failure that never crashes": the recovered
+ * gradient is g_scaled / S, computed in FP32 before the optimizer; any Inf or
+ * NaN means the step must be skipped.  Here: inv = fl32(1/S) once, then for
+ * every element y = fl32(fp32(g) * inv); the output is y, or the canonical
+ * quiet NaN 0x7FC00000 when y is NaN; *found_inf is set to 1 when any y is
+ * not finite.  The whole list is processed by one kernel launch.
+ *
+ *   n          number of tensors (>= 0).
+ *   grads      host array of n device pointers to FP16 gradients (2-byte
+ *              aligned; 16-byte alignment takes the vector path).
+ *   outs       host array of n device pointers to FP32 outputs (4-byte
+ *              aligned), each with room for numels[i] floats; an output must
+ *              not overlap any input or other output.
+ *   numels     host array of n element counts (>= 0; 0 is allowed).
+ *   in_dtype   must be GS_F16.
+ *   scale      device pointer to the current loss scale S (FP32), read only.
+ *   found_inf  device int32, only ever written with 1 (set-only: the caller
+ *              zeroes it once per step, several calls may OR into it, and
+ *              gs_update_scale consumes and clears it).
+ *   stream     hipStream_t.
+ * The device copy of the (pointer, size) list is cached by the library, so a
+ * repeated call with the same list uploads nothing.
+ */
+gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *outs,
+                           const int64_t *numels, gs_dtype in_dtype, const float *scale,
+                           int32_t *found_inf, void *stream);
+
+/*
+ * gs_update_scale -- grow/backoff/skip state machine, kept on the device.
+ * SimpleGradScaler.step ("Loss scaling, FP8, and the failure that never
+ * crashes", worked example) with the GradScaler defaults paragraph of
+ * "Numerical Precision, Mixed Precision, and Loss Scaling":
+ *   if *found_inf != 0:  S = fl32(S * backoff_factor); *growth_tracker = 0;
+ *                        *skip_count += 1 (when skip_count is not NULL)
+ *   else:                *growth_tracker += 1; if it reaches growth_interval,
+ *                        S = fl32(S * growth_factor) and *growth_tracker = 0
+ *   then *found_inf = 0.  No floor or ceiling: S may reach 0 or +Inf.
+ *
+ *   scale, growth_tracker, found_inf: device scalars (FP32, int32, int32).
+ *   growth_factor, backoff_factor: finite and > 0 (defaults 2.0, 0.5).
+ *   growth_interval: > 0 (default 2000).
+ *   skip_count: device int64 or NULL.
+ * One single-lane kernel on `stream`; no host synchronisation.
+ */
+gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_inf,
+                          float growth_factor, float backoff_factor, int32_t growth_interval,
+                          int64_t *skip_count, void *stream);
+
+/*
+ * fp8_quantize_workspace_size -- bytes of device workspace fp8_quantize
+ * needs for this shape and granularity in FP8_SCALE_FROM_AMAX mode (per-tensor
+ * needs a small buffer of partial maxima; block granularities need none).
+ * Returns 0 when no workspace is needed.
+ */
+size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g);
+
+/*
+ * fp8_quantize -- scaled, saturating, round-to-nearest-even cast to OCP FP8.
+ * fp8_scaling.py in "Mixed precision and FP8 training" (quant, per_tensor,
+ * per_block) and Failure 1 / "The seam" of "Why FP8 training is stable".
+ * The input is widened exactly to FP32; per block:
+ *   FROM_AMAX: amax = largest finite |x| in the block (0 if none);
+ *              s = fl32(max(amax, fl32(1e-12)) / MAX), written to scales.
+ *   GIVEN:     s = scales[block] (read).
+ *   code = NaN x  -> sign|0x7F;
+ *          else y = fl32(x / s) (IEEE division); NaN y -> 0x7F;
+ *          else clamp y to [-MAX, MAX] and round to the nearest FP8 value,
+ *          ties to an even last fraction bit, keeping the sign (also of 0).
+ *   MAX = 448 (E4M3) or 57344 (E5M2).  Dequantisation is decode(code) * s.
+ *
+ *   x          device, row-major rows x cols, GS_BF16 or GS_F32, 16-byte
+ *              aligned (GS_ERR_ALIGN otherwise).
+ *   rows, cols >= 0.  FP8_BLOCK_1x128 needs cols % 128 == 0;
+ *              FP8_BLOCK_128x128 needs rows % 128 == 0 and cols % 128 == 0
+ *              (GS_ERR_SHAPE otherwise).  Per-tensor takes any shape.
+ *   codes      device uint8, rows x cols row-major, 16-byte aligned (1x128
+ *              blocks run along the contiguous dimension).
+ *   scales     device FP32, one per block, row-major: [1] (per-tensor),
+ *              [rows][cols/128] (1x128) or [rows/128][cols/128] (128x128).
+ *              Written in FROM_AMAX mode, read in GIVEN mode.  A per-tensor
+ *              quantize of an empty matrix still writes scales[0].
+ *   nonfinite  device int32 or NULL; set to 1 when any input is NaN or Inf
+ *              (set-only, never cleared).
+ *   workspace  device buffer of at least fp8_quantize_workspace_size()
+ *              bytes (may be NULL when that is 0); contents need no
+ *              initialisation and are scratch.
+ *   stream     hipStream_t.
+ */
+gs_status fp8_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                       fp8_format fmt, fp8_granularity g, fp8_scale_mode mode,
+                       uint8_t *codes, float *scales, int32_t *nonfinite,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fp8_dequantize -- out = fl32(decode(code) * s) in FP32, the canonical NaN
+ * 0x7FC00000 where that is NaN ("Mixed precision and FP8 training",
+ * quant(): cast back to float and multiply by the scale).  E5M2 Inf codes
+ * give +-Inf * s.
+ *   codes      device uint8 rows x cols (16-byte aligned); scales device
+ *              FP32 in the layout of fp8_quantize (4-byte aligned); out device
+ *              FP32 rows x cols (16-byte aligned).
+ *   Shape rules as for fp8_quantize.
+ */
+gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
+                         fp8_granularity g, const float *scales, float *out, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *gs_status_string(gs_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_FP8_H */

@@ -1,0 +1,178 @@
+"""loss_scaling_fp8_amd -- dynamic loss scaling and FP8 scaled casting on
+AMD MI355X (gfx950).
+
+A thin ctypes binding over libgsfp8.so, whose C ABI is include/gs.h.  The
+functions here carry the same names as the C entry points and only marshal
+arguments (tensor data pointers, sizes, the current HIP stream); every step
+of the computation runs in the library's HIP kernels.  PyTorch is used for
+device memory and streams only.  There is no fallback: if the library is not
+built, or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgsfp8.so")
+
+GS_OK = 0
+GS_F16, GS_BF16, GS_F32 = 1, 2, 3
+FP8_E4M3, FP8_E5M2 = 0, 1
+FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
+FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
+
+EXPORTS = ("gs_unscale_check", "gs_update_scale", "fp8_quantize_workspace_size",
+           "fp8_quantize", "fp8_dequantize", "gs_status_string")
+
+_lib = None
+
+
+class GSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s returned %d (%s)" % (where, status, status_string(status)))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgsfp8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgsfp8.so is not built; run "
+                               "`python -m loss_scaling_fp8_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.gs_unscale_check.argtypes = [I32, P, P, P, ctypes.c_int, P, P, P]
+        L.gs_unscale_check.restype = I32
+        L.gs_update_scale.argtypes = [P, P, P, F, F, I32, P, P]
+        L.gs_update_scale.restype = I32
+        L.fp8_quantize_workspace_size.argtypes = [I64, I64, ctypes.c_int]
+        L.fp8_quantize_workspace_size.restype = ctypes.c_size_t
+        L.fp8_quantize.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, P, P, P, P, ctypes.c_size_t, P]
+        L.fp8_quantize.restype = I32
+        L.fp8_dequantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P]
+        L.fp8_dequantize.restype = I32
+        L.gs_status_string.argtypes = [I32]
+        L.gs_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gs_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != GS_OK:
+        raise GSError(status, where)
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def n_scales(rows: int, cols: int, gran: int) -> int:
+    if gran == FP8_PER_TENSOR:
+        return 1
+    if gran == FP8_BLOCK_1x128:
+        return rows * (cols // 128)
+    return (rows // 128) * (cols // 128)
+
+
+def scale_shape(rows: int, cols: int, gran: int) -> tuple:
+    if gran == FP8_PER_TENSOR:
+        return (1,)
+    if gran == FP8_BLOCK_1x128:
+        return (rows, cols // 128)
+    return (rows // 128, cols // 128)
+
+
+# ------------------------------------------------------------------ unscale
+def gs_unscale_check(grads: Sequence, outs: Sequence, scale, found_inf, stream=None) -> None:
+    """FP16 gradients -> FP32 outputs multiplied by fl32(1/S); found_inf set to
+    1 on any non-finite output.  One kernel launch for the whole list."""
+    import torch
+    n = len(grads)
+    if len(outs) != n:
+        raise ValueError("grads and outs differ in length")
+    for g, o in zip(grads, outs):
+        if g.dtype != torch.float16 or o.dtype != torch.float32:
+            raise TypeError("grads must be float16 and outs float32")
+        if o.numel() != g.numel() or not g.is_contiguous() or not o.is_contiguous():
+            raise ValueError("each out must be a contiguous float32 tensor of its grad's size")
+    arr_g = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
+    arr_o = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    arr_n = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
+    _check(lib().gs_unscale_check(n, arr_g, arr_o, arr_n, GS_F16, _ptr(scale), _ptr(found_inf),
+                                  _stream(stream)), "gs_unscale_check")
+
+
+def gs_update_scale(scale, growth_tracker, found_inf, growth_factor: float = 2.0,
+                    backoff_factor: float = 0.5, growth_interval: int = 2000,
+                    skip_count=None, stream=None) -> None:
+    """Grow/backoff/skip update of the device-resident loss scale."""
+    _check(lib().gs_update_scale(_ptr(scale), _ptr(growth_tracker), _ptr(found_inf),
+                                 float(growth_factor), float(backoff_factor),
+                                 int(growth_interval), _ptr(skip_count), _stream(stream)),
+           "gs_update_scale")
+
+
+# ------------------------------------------------------------------ FP8
+def fp8_quantize_workspace_size(rows: int, cols: int, gran: int) -> int:
+    return int(lib().fp8_quantize_workspace_size(int(rows), int(cols), int(gran)))
+
+
+def fp8_quantize(x, fmt: int, gran: int, mode: int = FP8_SCALE_FROM_AMAX, codes=None,
+                 scales=None, nonfinite=None, workspace=None, stream=None):
+    """Quantize a 2-D bfloat16/float32 CUDA tensor; returns (codes, scales).
+    codes is uint8 [rows, cols]; scales float32 in the block layout.  In
+    given-scale mode `scales` must be supplied."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if x.dtype == torch.bfloat16:
+        dt = GS_BF16
+    elif x.dtype == torch.float32:
+        dt = GS_F32
+    else:
+        raise TypeError("x must be bfloat16 or float32")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        if mode == FP8_SCALE_GIVEN:
+            raise ValueError("given-scale mode needs scales")
+        scales = torch.empty(scale_shape(rows, cols, gran), dtype=torch.float32, device=x.device)
+    ws_bytes = fp8_quantize_workspace_size(rows, cols, gran)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_quantize(_ptr(x), dt, rows, cols, int(fmt), int(gran), int(mode),
+                              _ptr(codes), _ptr(scales), _ptr(nonfinite), _ptr(workspace),
+                              ws_bytes if workspace is not None else 0, _stream(stream)),
+           "fp8_quantize")
+    return codes, scales
+
+
+def fp8_dequantize(codes, fmt: int, gran: int, scales, out=None, stream=None):
+    """decode(code) * s in float32; returns out [rows, cols]."""
+    import torch
+    if codes.dim() != 2 or codes.dtype != torch.uint8:
+        raise TypeError("codes must be a 2-D uint8 tensor")
+    rows, cols = codes.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    _check(lib().fp8_dequantize(_ptr(codes), rows, cols, int(fmt), int(gran), _ptr(scales),
+                                _ptr(out), _stream(stream)), "fp8_dequantize")
+    return out

@@ -1,0 +1,263 @@
+// api.hip -- the C ABI of libgsfp8 (declared in include/gs.h): argument
+// validation on the host, the cached device work lists of the multi-tensor
+// unscale, and dispatch to the kernels.  No entry point synchronises the
+// host or reads device memory; the only device allocation happens the first
+// time a given gradient list is seen (its work list is cached).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "gs.h"
+#include "gs_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+// ------------------------------------------------------------ work-list cache
+// Key: device id + the (input, output, numel) triplets.  Value: one device
+// allocation holding the WorkList arrays.  Least-recently-used eviction; an
+// evicted list may still be referenced by queued kernels, so eviction waits
+// for the device before freeing.
+struct CachedList {
+    void *dev = nullptr;
+    gsk::WorkList wl{};
+};
+
+constexpr size_t kCacheEntries = 64;
+
+struct ListCache {
+    std::mutex mu;
+    std::list<std::string> lru;   // front = most recent
+    std::unordered_map<std::string, std::pair<CachedList, std::list<std::string>::iterator>> map;
+};
+
+ListCache &cache() {
+    static ListCache *c = new ListCache();   // never destroyed (no teardown-order issues)
+    return *c;
+}
+
+std::string make_key(int device, int32_t n, const void *const *in, float *const *out,
+                     const int64_t *numel) {
+    std::string k;
+    k.resize(sizeof(int) + size_t(n) * 3 * sizeof(uint64_t));
+    char *p = &k[0];
+    std::memcpy(p, &device, sizeof(int));
+    p += sizeof(int);
+    for (int32_t i = 0; i < n; ++i) {
+        const uint64_t t[3] = {uint64_t(uintptr_t(in[i])), uint64_t(uintptr_t(out[i])),
+                               uint64_t(numel[i])};
+        std::memcpy(p, t, sizeof(t));
+        p += sizeof(t);
+    }
+    return k;
+}
+
+gs_status build_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
+                     CachedList &cl) {
+    // layout: chunk_begin[n+1] | in[n] | out[n] | numel[n] | vec_ok[n] (int32)
+    const size_t b_begin = 0;
+    const size_t b_in = b_begin + size_t(n + 1) * 8;
+    const size_t b_out = b_in + size_t(n) * 8;
+    const size_t b_numel = b_out + size_t(n) * 8;
+    const size_t b_vec = b_numel + size_t(n) * 8;
+    const size_t bytes = b_vec + size_t(n) * 4;
+    std::vector<unsigned char> host(bytes);
+    int64_t *begin = reinterpret_cast<int64_t *>(host.data() + b_begin);
+    uint64_t *hin = reinterpret_cast<uint64_t *>(host.data() + b_in);
+    uint64_t *hout = reinterpret_cast<uint64_t *>(host.data() + b_out);
+    int64_t *hnum = reinterpret_cast<int64_t *>(host.data() + b_numel);
+    int32_t *hvec = reinterpret_cast<int32_t *>(host.data() + b_vec);
+    int64_t acc = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        begin[i] = acc;
+        acc += (numel[i] + gsk::kUnscaleChunk - 1) / gsk::kUnscaleChunk;
+        hin[i] = uint64_t(uintptr_t(in[i]));
+        hout[i] = uint64_t(uintptr_t(out[i]));
+        hnum[i] = numel[i];
+        hvec[i] = ((uintptr_t(in[i]) | uintptr_t(out[i])) & 15u) == 0 ? 1 : 0;
+    }
+    begin[n] = acc;
+    void *dev = nullptr;
+    if (hipMalloc(&dev, bytes) != hipSuccess) return GS_ERR_HIP;
+    if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dev);
+        return GS_ERR_HIP;
+    }
+    unsigned char *d = static_cast<unsigned char *>(dev);
+    cl.dev = dev;
+    cl.wl.chunk_begin = reinterpret_cast<const int64_t *>(d + b_begin);
+    cl.wl.in = reinterpret_cast<const uint16_t *const *>(d + b_in);
+    cl.wl.out = reinterpret_cast<float *const *>(d + b_out);
+    cl.wl.numel = reinterpret_cast<const int64_t *>(d + b_numel);
+    cl.wl.vec_ok = reinterpret_cast<const int32_t *>(d + b_vec);
+    cl.wl.n = n;
+    cl.wl.total_chunks = acc;
+    return GS_OK;
+}
+
+gs_status get_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
+                   gsk::WorkList &wl) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return GS_ERR_HIP;
+    std::string key = make_key(device, n, in, out, numel);
+    ListCache &c = cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    auto it = c.map.find(key);
+    if (it != c.map.end()) {
+        c.lru.splice(c.lru.begin(), c.lru, it->second.second);
+        wl = it->second.first.wl;
+        return GS_OK;
+    }
+    CachedList cl;
+    const gs_status st = build_list(n, in, out, numel, cl);
+    if (st != GS_OK) return st;
+    if (c.map.size() >= kCacheEntries) {
+        const std::string &old = c.lru.back();
+        auto oit = c.map.find(old);
+        (void)hipDeviceSynchronize();        // queued kernels may still read it
+        (void)hipFree(oit->second.first.dev);
+        c.map.erase(oit);
+        c.lru.pop_back();
+    }
+    c.lru.push_front(key);
+    c.map.emplace(key, std::make_pair(cl, c.lru.begin()));
+    wl = cl.wl;
+    return GS_OK;
+}
+
+inline bool bad_enum_fmt(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
+inline bool bad_enum_gran(int g) {
+    return g != FP8_PER_TENSOR && g != FP8_BLOCK_1x128 && g != FP8_BLOCK_128x128;
+}
+
+gs_status check_shape(int64_t rows, int64_t cols, int gran) {
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return GS_ERR_SIZE;
+    if (rows * cols > kMaxElems) return GS_ERR_SIZE;
+    if (gran == FP8_BLOCK_1x128 && cols % 128 != 0) return GS_ERR_SHAPE;
+    if (gran == FP8_BLOCK_128x128 && (rows % 128 != 0 || cols % 128 != 0)) return GS_ERR_SHAPE;
+    return GS_OK;
+}
+
+int64_t num_scales(int64_t rows, int64_t cols, int gran) {
+    if (gran == FP8_PER_TENSOR) return 1;
+    if (gran == FP8_BLOCK_1x128) return rows * (cols / 128);
+    return (rows / 128) * (cols / 128);
+}
+
+inline bool misaligned(const void *p, uintptr_t a) { return (uintptr_t(p) & (a - 1)) != 0; }
+
+inline gs_status from_hip(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *outs,
+                           const int64_t *numels, gs_dtype in_dtype, const float *scale,
+                           int32_t *found_inf, void *stream) {
+    if (n < 0) return GS_ERR_SIZE;
+    if (in_dtype != GS_F16) return GS_ERR_DTYPE;
+    if (!scale || !found_inf) return GS_ERR_NULL;
+    if (misaligned(scale, 4) || misaligned(found_inf, 4)) return GS_ERR_ALIGN;
+    if (n == 0) return GS_OK;
+    if (!grads || !outs || !numels) return GS_ERR_NULL;
+    int64_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (numels[i] < 0 || numels[i] > kMaxElems) return GS_ERR_SIZE;
+        if (numels[i] > 0 && (!grads[i] || !outs[i])) return GS_ERR_NULL;
+        if (misaligned(grads[i], 2) || misaligned(outs[i], 4)) return GS_ERR_ALIGN;
+        total += numels[i];
+        if (total > kMaxElems * 64) return GS_ERR_SIZE;
+    }
+    if (total == 0) return GS_OK;
+    gsk::WorkList wl;
+    const gs_status st = get_list(n, grads, outs, numels, wl);
+    if (st != GS_OK) return st;
+    return from_hip(gsk::launch_unscale_check(wl, scale, found_inf,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_inf,
+                          float growth_factor, float backoff_factor, int32_t growth_interval,
+                          int64_t *skip_count, void *stream) {
+    if (!scale || !growth_tracker || !found_inf) return GS_ERR_NULL;
+    if (misaligned(scale, 4) || misaligned(growth_tracker, 4) || misaligned(found_inf, 4) ||
+        misaligned(skip_count, 8))
+        return GS_ERR_ALIGN;
+    if (!(std::isfinite(growth_factor) && growth_factor > 0.0f)) return GS_ERR_ARG;
+    if (!(std::isfinite(backoff_factor) && backoff_factor > 0.0f)) return GS_ERR_ARG;
+    if (growth_interval <= 0) return GS_ERR_ARG;
+    return from_hip(gsk::launch_update_scale(scale, growth_tracker, found_inf, growth_factor,
+                                             backoff_factor, growth_interval, skip_count,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g) {
+    (void)rows;
+    (void)cols;
+    return g == FP8_PER_TENSOR ? size_t(gsk::kPartialSlots) * sizeof(uint32_t) : 0;
+}
+
+gs_status fp8_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                       fp8_format fmt, fp8_granularity g, fp8_scale_mode mode, uint8_t *codes,
+                       float *scales, int32_t *nonfinite, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (x_dtype != GS_BF16 && x_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (bad_enum_fmt(fmt) || bad_enum_gran(g)) return GS_ERR_ARG;
+    if (mode != FP8_SCALE_FROM_AMAX && mode != FP8_SCALE_GIVEN) return GS_ERR_ARG;
+    gs_status st = check_shape(rows, cols, g);
+    if (st != GS_OK) return st;
+    const int64_t n = rows * cols;
+    if (n > 0 && (!x || !codes)) return GS_ERR_NULL;
+    if (num_scales(rows, cols, g) > 0 && !scales) return GS_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(scales, 4) ||
+        misaligned(nonfinite, 4))
+        return GS_ERR_ALIGN;
+    const bool need_ws = (g == FP8_PER_TENSOR && mode == FP8_SCALE_FROM_AMAX);
+    if (need_ws) {
+        if (!workspace || workspace_bytes < fp8_quantize_workspace_size(rows, cols, g))
+            return GS_ERR_WORKSPACE;
+        if (misaligned(workspace, 4)) return GS_ERR_ALIGN;
+    }
+    return from_hip(gsk::launch_quantize(x, x_dtype, rows, cols, fmt, g, mode, codes, scales,
+                                         nonfinite, static_cast<uint32_t *>(workspace),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
+                         fp8_granularity g, const float *scales, float *out, void *stream) {
+    if (bad_enum_fmt(fmt) || bad_enum_gran(g)) return GS_ERR_ARG;
+    gs_status st = check_shape(rows, cols, g);
+    if (st != GS_OK) return st;
+    const int64_t n = rows * cols;
+    if (n > 0 && (!codes || !out || !scales)) return GS_ERR_NULL;
+    if (misaligned(codes, 16) || misaligned(out, 16) || misaligned(scales, 4)) return GS_ERR_ALIGN;
+    if (n == 0) return GS_OK;
+    return from_hip(gsk::launch_dequantize(codes, rows, cols, fmt, g, scales, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+const char *gs_status_string(gs_status status) {
+    switch (status) {
+        case GS_OK: return "GS_OK";
+        case GS_ERR_NULL: return "GS_ERR_NULL: a required pointer is NULL";
+        case GS_ERR_SIZE: return "GS_ERR_SIZE: negative or too large count or size";
+        case GS_ERR_SHAPE: return "GS_ERR_SHAPE: block granularity does not divide the shape";
+        case GS_ERR_DTYPE: return "GS_ERR_DTYPE: unsupported element type";
+        case GS_ERR_ARG: return "GS_ERR_ARG: bad enum, factor or interval";
+        case GS_ERR_ALIGN: return "GS_ERR_ALIGN: misaligned pointer";
+        case GS_ERR_WORKSPACE: return "GS_ERR_WORKSPACE: workspace missing or too small";
+        case GS_ERR_HIP: return "GS_ERR_HIP: HIP runtime or launch failure";
+        default: return "unknown gs_status";
+    }
+}
+
+}  // extern "C"

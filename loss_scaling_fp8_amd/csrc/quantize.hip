@@ -1,0 +1,483 @@
+// quantize.hip -- FP8 (OCP E4M3 / E5M2) scaled quantization at per-tensor,
+// 1x128 and 128x128 granularity, and the matching dequantization.
+//
+// What is computed ("Mixed precision and FP8 training", section "FP8
+// training", fp8_scaling.py: quant / per_tensor / per_block; "Why FP8
+// training is stable", Failure 1 and "The seam"): per block, the largest
+// finite |x| gives s = fl32(max(amax, 1e-12) / MAX); each element becomes
+// the FP8 code of clamp(fl32(x / s), -MAX, MAX) rounded to nearest-even; the
+// dequantized value is decode(code) * s in FP32.
+//
+// Design (gfx950, wave64):
+//  * 1x128: a row-major matrix whose width is a multiple of 128 is a flat
+//    sequence of 128-element blocks, so the kernel walks blocks linearly.
+//    A lane owns 32 contiguous elements (4 x 16-byte loads of BF16), a quad
+//    of lanes owns a block: the block amax is two DPP quad exchanges, and
+//    each lane stores 32 codes (2 x 16 bytes).
+//  * 128x128: one 256-lane workgroup per tile, the whole tile held in
+//    registers (64 elements per lane); amax by DPP inside rows of 16 lanes,
+//    two cross-row shuffles, and 4 LDS words across the waves.
+//  * per-tensor: the scale depends on the whole tensor, so two launches: a
+//    persistent pass writes one partial max per workgroup (no atomics, no
+//    zero-initialised memory), then the cast pass reduces the <= 1024
+//    partials in every workgroup and streams the tensor again.
+//  * Division: x / s is formed from r = fl32(1/s) and one FMA correction
+//    (div_by_scale) whenever s is in the range where that reproduces the
+//    IEEE quotient's FP8 code, else by IEEE division.  Lanes holding a NaN
+//    or Inf take the exact per-element path; amax ignores them.
+//  * The max-abs is taken on bit patterns: for non-negative floats unsigned
+//    integer order is numeric order, and BF16 halves are maxed pairwise.
+#include "device_fp8.hpp"
+#include "gs_internal.hpp"
+
+namespace gsk {
+
+namespace {
+
+constexpr uint32_t kFloorBits = 0x2B8CBCCCu;  // fl32(1e-12)
+
+template <int FMT>
+__device__ __forceinline__ float scale_from_amax(float amax) {
+    const float fl = as_f32(kFloorBits);
+    const float a = amax > fl ? amax : fl;
+    return a / Fp8<FMT>::kMax;
+}
+
+// ---------------------------------------------------------------- lane data
+// NV 16-byte vectors of input per lane, as 32-bit words.
+template <typename IN, int NV>
+struct LaneData {
+    static constexpr int kPerVec = 16 / int(sizeof(IN));   // elements per vector
+    static constexpr int kElems = NV * kPerVec;
+    static constexpr int kWords = NV * 4;
+    uint32_t w[kWords];
+
+    __device__ __forceinline__ void load(const IN *p) {
+        const uint4 *v = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint4 t = v[i];
+            w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+        }
+    }
+    // load NV vectors spaced `stride` elements apart
+    __device__ __forceinline__ void load_strided(const IN *p, int64_t stride) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint4 t = *reinterpret_cast<const uint4 *>(p + i * stride);
+            w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+        }
+    }
+
+    // FP32 bit pattern of element i (BF16 widened by appending 16 zeros)
+    __device__ __forceinline__ uint32_t elem(int i) const {
+        if constexpr (sizeof(IN) == 2)
+            return (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
+        else
+            return w[i];
+    }
+
+    // Largest finite |x| of the lane as FP32 bits; returns true when the lane
+    // holds a NaN or an Inf (those are left out of the max).
+    __device__ __forceinline__ bool absmax(uint32_t &amax_bits) const {
+        if constexpr (sizeof(IN) == 2) {
+            typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+            us2 m = {0, 0};
+#pragma unroll
+            for (int i = 0; i < kWords; ++i)
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
+            uint32_t m16 = m.x > m.y ? m.x : m.y;
+            const bool nf = m16 >= 0x7F80u;
+            if (nf) {
+                m16 = 0;
+#pragma unroll
+                for (int i = 0; i < kWords; ++i) {
+                    const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+                    if (lo < 0x7F80u && lo > m16) m16 = lo;
+                    if (hi < 0x7F80u && hi > m16) m16 = hi;
+                }
+            }
+            amax_bits = m16 << 16;
+            return nf;
+        } else {
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < kWords; ++i) m = max(m, w[i] & 0x7FFFFFFFu);
+            const bool nf = m >= 0x7F800000u;
+            if (nf) {
+                m = 0;
+#pragma unroll
+                for (int i = 0; i < kWords; ++i) {
+                    const uint32_t a = w[i] & 0x7FFFFFFFu;
+                    if (a < 0x7F800000u && a > m) m = a;
+                }
+            }
+            amax_bits = m;
+            return nf;
+        }
+    }
+
+    // FP8 codes of all lane elements, 4 per output word (little-endian).
+    template <int FMT>
+    __device__ __forceinline__ void cast(float s, bool lane_nonfinite,
+                                         uint32_t (&out)[kElems / 4]) const {
+        const float r = 1.0f / s;
+        if (fast_scale(s) && !lane_nonfinite) {
+#pragma unroll
+            for (int j = 0; j < kElems / 4; ++j) {
+                uint32_t acc = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t e = elem(4 * j + k);
+                    const float q = div_by_scale(as_f32(e & 0x7FFFFFFFu), s, r);
+                    const uint32_t c = encode_mag<FMT>(as_u32(q)) | ((e >> 24) & 0x80u);
+                    acc |= c << (8 * k);
+                }
+                out[j] = acc;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kElems / 4; ++j) {
+                uint32_t acc = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    acc |= cast_exact<FMT>(as_f32(elem(4 * j + k)), s) << (8 * k);
+                out[j] = acc;
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ void store_words(uint8_t *p, const uint32_t *w, int nwords) {
+    // nwords is a compile-time multiple of 1..4 words; 16-byte pieces first
+    int i = 0;
+    for (; i + 4 <= nwords; i += 4)
+        *reinterpret_cast<uint4 *>(p + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+    for (; i + 2 <= nwords; i += 2)
+        *reinterpret_cast<uint2 *>(p + 4 * i) = make_uint2(w[i], w[i + 1]);
+    for (; i < nwords; ++i) *reinterpret_cast<uint32_t *>(p + 4 * i) = w[i];
+}
+
+// ---------------------------------------------------------------- 1x128
+// Lanes per block: 4; each lane 32 elements (BF16: 4 vectors, FP32: 8).
+template <int FMT, int MODE, typename IN>
+__global__ __launch_bounds__(256)
+void quant_1x128_kernel(const IN *__restrict__ x, int64_t nblocks, uint8_t *__restrict__ codes,
+                        float *__restrict__ scales, int32_t *__restrict__ nonfinite) {
+    constexpr int kLanesPerBlock = 4;
+    constexpr int kElems = 128 / kLanesPerBlock;             // 32
+    constexpr int NV = kElems * int(sizeof(IN)) / 16;
+    constexpr int kBlocksPerWG = 256 / kLanesPerBlock;       // 64
+    const int sub = threadIdx.x & (kLanesPerBlock - 1);
+    bool saw_nf = false;
+    for (int64_t b = int64_t(blockIdx.x) * kBlocksPerWG + (threadIdx.x / kLanesPerBlock);
+         b < nblocks; b += int64_t(gridDim.x) * kBlocksPerWG) {
+        LaneData<IN, NV> L;
+        L.load(x + b * 128 + sub * kElems);
+        uint32_t amax_bits;
+        const bool nf = L.absmax(amax_bits);
+        saw_nf |= nf;
+        float s;
+        if (MODE == FP8_SCALE_FROM_AMAX) {
+            amax_bits = group_max<kLanesPerBlock>(amax_bits);
+            s = scale_from_amax<FMT>(as_f32(amax_bits));
+            if (sub == 0) scales[b] = s;
+        } else {
+            s = scales[b];
+        }
+        uint32_t out[kElems / 4];
+        L.template cast<FMT>(s, nf, out);
+        store_words(codes + b * 128 + sub * kElems, out, kElems / 4);
+    }
+    if (saw_nf && nonfinite) *nonfinite = 1;
+}
+
+// ---------------------------------------------------------------- 128x128
+// One workgroup per tile.  Threads per 128-element row: 16 (BF16) or 32
+// (FP32), one 16-byte vector each; the tile takes 8 or 16 row passes.
+template <int FMT, int MODE, typename IN>
+__global__ __launch_bounds__(256)
+void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_per_row,
+                          int64_t ntiles, uint8_t *__restrict__ codes, float *__restrict__ scales,
+                          int32_t *__restrict__ nonfinite) {
+    constexpr int kPerVec = 16 / int(sizeof(IN));
+    constexpr int kThreadsPerRow = 128 / kPerVec;
+    constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+    constexpr int kPasses = 128 / kRowsPerPass;
+    __shared__ uint32_t red[4];
+    const int tid = threadIdx.x;
+    const int row0 = tid / kThreadsPerRow;
+    const int seg = tid % kThreadsPerRow;
+    bool saw_nf = false;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t ti = t / tiles_per_row, tj = t - ti * tiles_per_row;
+        const int64_t base = (ti * 128 + row0) * cols + tj * 128 + seg * kPerVec;
+        LaneData<IN, kPasses> L;
+        L.load_strided(x + base, int64_t(kRowsPerPass) * cols);
+        uint32_t amax_bits;
+        const bool nf = L.absmax(amax_bits);
+        saw_nf |= nf;
+        float s;
+        if (MODE == FP8_SCALE_FROM_AMAX) {
+            amax_bits = wave_max(amax_bits);
+            if ((tid & 63) == 0) red[tid >> 6] = amax_bits;
+            __syncthreads();
+            amax_bits = max(max(red[0], red[1]), max(red[2], red[3]));
+            __syncthreads();                  // red[] is reused by the next tile
+            s = scale_from_amax<FMT>(as_f32(amax_bits));
+            if (tid == 0) scales[t] = s;
+        } else {
+            s = scales[t];
+        }
+        uint32_t out[LaneData<IN, kPasses>::kElems / 4];
+        L.template cast<FMT>(s, nf, out);
+        // each pass contributes kPerVec codes of one row
+        constexpr int kWordsPerPass = kPerVec / 4;
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            uint8_t *dst = codes + base + int64_t(p) * kRowsPerPass * cols;
+            if constexpr (kWordsPerPass == 2)
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(out[2 * p], out[2 * p + 1]);
+            else
+                *reinterpret_cast<uint32_t *>(dst) = out[p];
+        }
+    }
+    if (saw_nf && nonfinite) *nonfinite = 1;
+}
+
+// ---------------------------------------------------------------- per-tensor
+// Pass 1: one partial finite max (FP32 bits) per workgroup.
+template <typename IN>
+__global__ __launch_bounds__(256)
+void amax_partials_kernel(const IN *__restrict__ x, int64_t n, uint32_t *__restrict__ partials,
+                          int32_t *__restrict__ nonfinite) {
+    constexpr int kPerVec = 16 / int(sizeof(IN));
+    constexpr int kUnroll = 4;
+    __shared__ uint32_t red[4];
+    const int64_t nvec = n / kPerVec;
+    uint32_t m = 0;
+    bool nf = false;
+    const int64_t step = int64_t(gridDim.x) * 256;
+    for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec; v += kUnroll * step) {
+        LaneData<IN, 1> L[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (v + u * step < nvec) L[u].load(x + (v + u * step) * kPerVec);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (v + u * step < nvec) {
+                uint32_t a;
+                nf |= L[u].absmax(a);
+                m = max(m, a);
+            }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
+        const IN *p = x + nvec * kPerVec + threadIdx.x;
+        uint32_t b;
+        if constexpr (sizeof(IN) == 2) b = uint32_t(*reinterpret_cast<const uint16_t *>(p)) << 16;
+        else b = *reinterpret_cast<const uint32_t *>(p);
+        b &= 0x7FFFFFFFu;
+        if (b >= 0x7F800000u) nf = true; else m = max(m, b);
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (nf && nonfinite) *nonfinite = 1;
+}
+
+// Pass 2 (or the only pass in given-scale mode): cast with one scale.
+template <int FMT, int MODE, typename IN>
+__global__ __launch_bounds__(256)
+void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, const uint32_t *__restrict__ partials,
+                         int nparts, uint8_t *__restrict__ codes, float *__restrict__ scales,
+                         int32_t *__restrict__ nonfinite) {
+    constexpr int kPerVec = 16 / int(sizeof(IN));
+    __shared__ uint32_t red[4];
+    float s;
+    if (MODE == FP8_SCALE_FROM_AMAX) {
+        uint32_t m = 0;
+        for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, partials[i]);
+        m = wave_max(m);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        s = scale_from_amax<FMT>(as_f32(m));
+        if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
+    } else {
+        s = scales[0];
+    }
+    bool saw_nf = false;
+    const int64_t nvec = n / kPerVec;
+    for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+         v += int64_t(gridDim.x) * 256) {
+        LaneData<IN, 1> L;
+        L.load(x + v * kPerVec);
+        uint32_t a;
+        const bool nf = L.absmax(a);
+        saw_nf |= nf;
+        uint32_t out[kPerVec / 4];
+        L.template cast<FMT>(s, nf, out);
+        store_words(codes + v * kPerVec, out, kPerVec / 4);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
+        const int64_t i = nvec * kPerVec + threadIdx.x;
+        uint32_t b;
+        if constexpr (sizeof(IN) == 2) b = uint32_t(reinterpret_cast<const uint16_t *>(x)[i]) << 16;
+        else b = reinterpret_cast<const uint32_t *>(x)[i];
+        if ((b & 0x7FFFFFFFu) >= 0x7F800000u) saw_nf = true;
+        codes[i] = (uint8_t)cast_exact<FMT>(as_f32(b), s);
+    }
+    if (saw_nf && nonfinite) *nonfinite = 1;
+}
+
+// ---------------------------------------------------------------- dequantize
+// 16 codes per lane-step -> 16 FP32 (4 x 16-byte stores).
+template <int FMT>
+__device__ __forceinline__ void dequant16(uint4 c, float s, float4 *dst) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v[b] = canon(decode<FMT>((w[k] >> (8 * b)) & 0xFFu) * s);
+        dst[k] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// per-tensor (BLOCKED = false) or 1x128 (BLOCKED = true): flat walk
+template <int FMT, bool BLOCKED>
+__global__ __launch_bounds__(256)
+void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
+                           const float *__restrict__ scales, float *__restrict__ out) {
+    const int64_t nvec = n / 16;
+    const float s0 = BLOCKED ? 0.0f : scales[0];
+    for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+         v += int64_t(gridDim.x) * 256) {
+        const uint4 c = reinterpret_cast<const uint4 *>(codes)[v];
+        const float s = BLOCKED ? scales[v >> 3] : s0;       // 8 vectors per 128-block
+        dequant16<FMT>(c, s, reinterpret_cast<float4 *>(out + v * 16));
+    }
+    if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - nvec * 16) {
+        const int64_t i = nvec * 16 + threadIdx.x;
+        out[i] = canon(decode<FMT>(codes[i]) * s0);
+    }
+}
+
+// 128x128: one workgroup per tile; 8 lanes per row (16 codes each),
+// 32 rows per pass, 4 passes.
+template <int FMT>
+__global__ __launch_bounds__(256)
+void dequant_128x128_kernel(const uint8_t *__restrict__ codes, int64_t cols,
+                            int64_t tiles_per_row, int64_t ntiles,
+                            const float *__restrict__ scales, float *__restrict__ out) {
+    const int row0 = threadIdx.x >> 3, seg = threadIdx.x & 7;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t ti = t / tiles_per_row, tj = t - ti * tiles_per_row;
+        const float s = scales[t];
+        uint4 c[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            c[p] = *reinterpret_cast<const uint4 *>(
+                codes + (ti * 128 + row0 + 32 * p) * cols + tj * 128 + seg * 16);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            dequant16<FMT>(c[p], s, reinterpret_cast<float4 *>(
+                out + (ti * 128 + row0 + 32 * p) * cols + tj * 128 + seg * 16));
+    }
+}
+
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+
+inline uint32_t grid_for(int64_t work_items, int64_t per_wg) {
+    int64_t g = (work_items + per_wg - 1) / per_wg;
+    if (g < 1) g = 1;
+    if (g > kMaxGrid) g = kMaxGrid;
+    return (uint32_t)g;
+}
+
+template <int FMT, int MODE, typename IN>
+hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uint8_t *codes,
+                          float *scales, int32_t *nonfinite, uint32_t *partials,
+                          hipStream_t stream) {
+    const int64_t n = rows * cols;
+    if (gran == FP8_BLOCK_1x128) {
+        const int64_t nblocks = n / 128;
+        if (nblocks == 0) return hipSuccess;
+        hipLaunchKernelGGL((quant_1x128_kernel<FMT, MODE, IN>), dim3(grid_for(nblocks, 64)),
+                           dim3(256), 0, stream, x, nblocks, codes, scales, nonfinite);
+        return hipGetLastError();
+    }
+    if (gran == FP8_BLOCK_128x128) {
+        const int64_t tpr = cols / 128, ntiles = (rows / 128) * tpr;
+        if (ntiles == 0) return hipSuccess;
+        hipLaunchKernelGGL((quant_128x128_kernel<FMT, MODE, IN>), dim3(grid_for(ntiles, 1)),
+                           dim3(256), 0, stream, x, cols, tpr, ntiles, codes, scales, nonfinite);
+        return hipGetLastError();
+    }
+    // per-tensor
+    constexpr int kPerVec = 16 / int(sizeof(IN));
+    int nparts = 0;
+    if (MODE == FP8_SCALE_FROM_AMAX) {
+        int64_t p = (n / kPerVec + 256 * 16 - 1) / (256 * 16);     // >= 16 vectors per lane
+        if (p < 1) p = 1;
+        if (p > kPartialSlots) p = kPartialSlots;
+        nparts = (int)p;
+        hipLaunchKernelGGL((amax_partials_kernel<IN>), dim3(nparts), dim3(256), 0, stream, x, n,
+                           partials, nonfinite);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((quant_tensor_kernel<FMT, MODE, IN>),
+                       dim3(grid_for(n / kPerVec, 256 * 4)), dim3(256), 0, stream, x, n,
+                       partials, nparts, codes, scales, nonfinite);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int gran,
+                          const float *scales, float *out, hipStream_t stream) {
+    const int64_t n = rows * cols;
+    if (gran == FP8_BLOCK_128x128) {
+        const int64_t tpr = cols / 128, ntiles = (rows / 128) * tpr;
+        if (ntiles == 0) return hipSuccess;
+        hipLaunchKernelGGL((dequant_128x128_kernel<FMT>), dim3(grid_for(ntiles, 1)), dim3(256),
+                           0, stream, codes, cols, tpr, ntiles, scales, out);
+        return hipGetLastError();
+    }
+    if (n == 0) return hipSuccess;
+    if (gran == FP8_BLOCK_1x128)
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, true>), dim3(grid_for(n / 16, 256 * 4)),
+                           dim3(256), 0, stream, codes, n, scales, out);
+    else
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, false>), dim3(grid_for(n / 16, 256 * 4)),
+                           dim3(256), 0, stream, codes, n, scales, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *x, gs_dtype dt, int64_t rows, int64_t cols, int fmt,
+                           int gran, int mode, uint8_t *codes, float *scales,
+                           int32_t *nonfinite, uint32_t *partials, hipStream_t stream) {
+#define GS_Q(F, M, T) \
+    return quantize_typed<F, M, T>(static_cast<const T *>(x), rows, cols, gran, codes, scales, \
+                                   nonfinite, partials, stream)
+#define GS_Q_T(F, M) \
+    if (dt == GS_BF16) GS_Q(F, M, uint16_t); else GS_Q(F, M, float)
+    if (fmt == FP8_E4M3) {
+        if (mode == FP8_SCALE_FROM_AMAX) { GS_Q_T(0, 0); } else { GS_Q_T(0, 1); }
+    } else {
+        if (mode == FP8_SCALE_FROM_AMAX) { GS_Q_T(1, 0); } else { GS_Q_T(1, 1); }
+    }
+#undef GS_Q_T
+#undef GS_Q
+}
+
+hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
+                             const float *scales, float *out, hipStream_t stream) {
+    if (fmt == FP8_E4M3) return dequantize_fmt<0>(codes, rows, cols, gran, scales, out, stream);
+    return dequantize_fmt<1>(codes, rows, cols, gran, scales, out, stream);
+}
+
+}  // namespace gsk

@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI library: it loads, exports every function that
+include/gs.h declares, and rejects bad arguments on the host (returning the
+documented status before anything touches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import loss_scaling_fp8_amd as gs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                                r"([a-z][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_api():
+    assert set(_declared_functions()) == set(gs.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = gs.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code, name in ((0, "GS_OK"), (-1, "GS_ERR_NULL"), (-3, "GS_ERR_SHAPE"),
+                       (-7, "GS_ERR_WORKSPACE"), (-8, "GS_ERR_HIP")):
+        assert gs.status_string(code).startswith(name)
+    assert "unknown" in gs.status_string(12345)
+
+
+def test_workspace_size():
+    assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_PER_TENSOR) == 4096
+    assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_BLOCK_1x128) == 0
+    assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_BLOCK_128x128) == 0
+
+
+# Argument errors are found before any HIP call, so they are testable here.
+FAKE = 1 << 40          # an aligned, never-dereferenced "device" address
+
+
+def test_unscale_argument_errors():
+    L = gs.lib()
+    one = (ctypes.c_void_p * 1)(FAKE)
+    n5 = (ctypes.c_int64 * 1)(5)
+    assert L.gs_unscale_check(-1, one, one, n5, gs.GS_F16, FAKE, FAKE, None) == -2
+    assert L.gs_unscale_check(1, one, one, n5, gs.GS_BF16, FAKE, FAKE, None) == -4
+    assert L.gs_unscale_check(1, one, one, n5, gs.GS_F16, None, FAKE, None) == -1
+    assert L.gs_unscale_check(1, one, one, n5, gs.GS_F16, FAKE, None, None) == -1
+    assert L.gs_unscale_check(1, None, one, n5, gs.GS_F16, FAKE, FAKE, None) == -1
+    nul = (ctypes.c_void_p * 1)(None)
+    assert L.gs_unscale_check(1, nul, one, n5, gs.GS_F16, FAKE, FAKE, None) == -1
+    neg = (ctypes.c_int64 * 1)(-3)
+    assert L.gs_unscale_check(1, one, one, neg, gs.GS_F16, FAKE, FAKE, None) == -2
+    odd = (ctypes.c_void_p * 1)(FAKE + 1)
+    assert L.gs_unscale_check(1, odd, one, n5, gs.GS_F16, FAKE, FAKE, None) == -6
+    assert L.gs_unscale_check(1, one, odd, n5, gs.GS_F16, FAKE, FAKE, None) == -6
+    # nothing to do: returns OK without launching
+    assert L.gs_unscale_check(0, None, None, None, gs.GS_F16, FAKE, FAKE, None) == 0
+    zero = (ctypes.c_int64 * 1)(0)
+    assert L.gs_unscale_check(1, nul, nul, zero, gs.GS_F16, FAKE, FAKE, None) == 0
+
+
+def test_update_argument_errors():
+    L = gs.lib()
+    assert L.gs_update_scale(None, FAKE, FAKE, 2.0, 0.5, 2000, None, None) == -1
+    assert L.gs_update_scale(FAKE, FAKE, FAKE, 2.0, 0.5, 0, None, None) == -5
+    assert L.gs_update_scale(FAKE, FAKE, FAKE, float("inf"), 0.5, 10, None, None) == -5
+    assert L.gs_update_scale(FAKE, FAKE, FAKE, 2.0, -0.5, 10, None, None) == -5
+    assert L.gs_update_scale(FAKE, FAKE, FAKE, 2.0, 0.0, 10, None, None) == -5
+    assert L.gs_update_scale(FAKE + 2, FAKE, FAKE, 2.0, 0.5, 10, None, None) == -6
+    assert L.gs_update_scale(FAKE, FAKE, FAKE, 2.0, 0.5, 10, FAKE + 4, None) == -6
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, 1, 128, 128, 0, 1, 0), -4),        # FP16 input not supported
+    ((FAKE, 2, 128, 128, 2, 1, 0), -5),        # bad format
+    ((FAKE, 2, 128, 128, 0, 3, 0), -5),        # bad granularity
+    ((FAKE, 2, 128, 128, 0, 1, 2), -5),        # bad mode
+    ((FAKE, 2, 128, 100, 0, 1, 0), -3),        # 1x128 needs cols % 128
+    ((FAKE, 2, 100, 128, 0, 2, 0), -3),        # 128x128 needs rows % 128
+    ((FAKE, 2, -1, 128, 0, 0, 0), -2),
+    ((FAKE, 2, 1 << 32, 2, 0, 0, 0), -2),
+    ((None, 2, 128, 128, 0, 1, 0), -1),
+    ((FAKE + 2, 2, 128, 128, 0, 1, 0), -6),
+])
+def test_quantize_argument_errors(args, code):
+    L = gs.lib()
+    x, dt, r, c, fmt, gran, mode = args
+    assert L.fp8_quantize(x, dt, r, c, fmt, gran, mode, FAKE, FAKE, None, None, 0, None) == code
+
+
+def test_quantize_workspace_and_output_errors():
+    L = gs.lib()
+    # per-tensor amax mode without workspace
+    assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, FAKE, FAKE, None, None, 0, None) == -7
+    assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, FAKE, FAKE, None, FAKE, 16, None) == -7
+    assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, None, FAKE, None, FAKE, 4096, None) == -1
+    assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, FAKE, None, None, FAKE, 4096, None) == -1
+
+
+def test_dequantize_argument_errors():
+    L = gs.lib()
+    assert L.fp8_dequantize(FAKE, 128, 100, 0, 1, FAKE, FAKE, None) == -3
+    assert L.fp8_dequantize(FAKE, 128, 128, 5, 1, FAKE, FAKE, None) == -5
+    assert L.fp8_dequantize(None, 128, 128, 0, 1, FAKE, FAKE, None) == -1
+    assert L.fp8_dequantize(FAKE, 128, 128, 0, 1, FAKE, FAKE + 8, None) == -6
+    assert L.fp8_dequantize(None, 0, 128, 0, 1, None, None, None) == 0   # empty: nothing to do

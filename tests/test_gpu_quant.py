@@ -1,0 +1,182 @@
+"""GPU parity: FP8 quantize / dequantize through the C ABI, bit for bit
+against the oracle (codes, scales, dequantized FP32, the nonfinite flag)."""
+import numpy as np
+import pytest
+import torch
+
+import loss_scaling_fp8_amd as gs
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = gs.FP8_E4M3, gs.FP8_E5M2
+PT, B1, B128 = gs.FP8_PER_TENSOR, gs.FP8_BLOCK_1x128, gs.FP8_BLOCK_128x128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda:0")
+
+
+def _u32(t):
+    return t.detach().cpu().contiguous().numpy().reshape(-1).view(np.uint32)
+
+
+def _special_bf16(rng, rows, cols):
+    """BF16 bit patterns: N(0,1)-ish body with planted NaN (both signs,
+    payloads), +-Inf, +-0, BF16 subnormals, huge values, values above 448 and
+    57344, and exact E4M3/E5M2 midpoints at s = 1."""
+    x = (rng.standard_normal((rows, cols)) * 3).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    n = rows * cols
+    flat = bits.reshape(-1)
+    pos = rng.permutation(n)
+    k = max(1, n // 50)
+    specials = [
+        lambda m: 0x7FC0 | rng.integers(0, 0x3F, m).astype(np.uint16),          # +NaN
+        lambda m: 0xFF80 | rng.integers(1, 0x7F, m).astype(np.uint16),          # -NaN
+        lambda m: np.full(m, 0x7F80, np.uint16), lambda m: np.full(m, 0xFF80, np.uint16),
+        lambda m: np.full(m, 0x0000, np.uint16), lambda m: np.full(m, 0x8000, np.uint16),
+        lambda m: rng.integers(1, 0x80, m).astype(np.uint16),                   # subnormals
+        lambda m: rng.integers(0x7000, 0x7F80, m).astype(np.uint16),            # huge
+        lambda m: rng.integers(0x43E0, 0x43F8, m).astype(np.uint16),            # ~448..496
+        lambda m: rng.integers(0x4760, 0x4778, m).astype(np.uint16),            # ~57344..63488
+        lambda m: (0x3C00 + (rng.integers(0, 120, m) << 4 | 0x8)).astype(np.uint16),  # E4M3 mids
+        lambda m: (0x3800 + (rng.integers(0, 240, m) << 5 | 0x10)).astype(np.uint16),  # E5M2 mids
+    ]
+    for j, f in enumerate(specials):
+        idx = pos[j * k:(j + 1) * k]
+        flat[idx] = f(idx.size) | (flat[idx] & 0x8000 if j >= 6 else 0)
+    return bits
+
+
+def _run(x_host, fmt, gran, mode, dev, scales_host=None):
+    """x_host: float32 array or uint16 BF16 bits [rows, cols]."""
+    if x_host.dtype == np.uint16:
+        x = torch.from_numpy(x_host.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(x_host).to(dev)
+    rows, cols = x_host.shape
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    sc = None
+    if scales_host is not None:
+        sc = torch.from_numpy(scales_host.astype(np.float32)).to(dev).reshape(
+            gs.scale_shape(rows, cols, gran))
+    codes, scales = gs.fp8_quantize(x, fmt, gran, mode, scales=sc, nonfinite=nf)
+    deq = gs.fp8_dequantize(codes, fmt, gran, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), _u32(scales), _u32(deq), int(nf.item())
+
+
+def _check(x_host, fmt, gran, mode, dev, scales_host=None):
+    c, s, d, nf = _run(x_host, fmt, gran, mode, dev, scales_host)
+    rc, rs, rnf = oracle.quantize(x_host, fmt, gran, mode, scales_host)
+    rd = oracle.dequantize(rc, fmt, gran, rs)
+    if not np.array_equal(c, rc):
+        bad = np.argwhere(c != rc)[:5]
+        raise AssertionError("codes differ at %s: gpu %s oracle %s" % (
+            bad.tolist(), [hex(c[tuple(b)]) for b in bad], [hex(rc[tuple(b)]) for b in bad]))
+    assert np.array_equal(s, rs.view(np.uint32)), "scales differ"
+    assert np.array_equal(d, rd.reshape(-1).view(np.uint32)), "dequantized values differ"
+    assert nf == rnf
+
+
+SHAPES = {PT: [(1, 1), (3, 5), (7, 129), (1000, 999), (1024, 1024)],
+          B1: [(1, 128), (3, 384), (130, 256), (257, 640)],
+          B128: [(128, 128), (256, 384), (384, 640)]}
+
+
+@pytest.mark.parametrize("gran", [PT, B1, B128])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_special_values_all_shapes(gran, fmt, dtype, dev):
+    rng = np.random.default_rng(1000 + 10 * gran + fmt)
+    for rows, cols in SHAPES[gran]:
+        bits = _special_bf16(rng, rows, cols)
+        x = bits if dtype == "bf16" else (bits.astype(np.uint32) << 16).view(np.float32)
+        _check(np.ascontiguousarray(x), fmt, gran, gs.FP8_SCALE_FROM_AMAX, dev)
+
+
+@pytest.mark.parametrize("gran", [PT, B1, B128])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_given_scales_including_degenerate(gran, fmt, dev):
+    rng = np.random.default_rng(77 + gran + 3 * fmt)
+    rows, cols = (256, 384) if gran != PT else (300, 77)
+    bits = _special_bf16(rng, rows, cols)
+    ns = oracle.n_scales(rows, cols, gran)
+    pool = np.float32([1.0, 0.5, 3.0, 1e-3, 1e-30, 2.0 ** -90, 1e36, 3e38, 0.0, -0.0, -2.0,
+                       np.inf, np.nan, 1e-45, 2.0 ** -126, 7.25])
+    for trial in range(4):
+        sc = pool[rng.integers(0, pool.size, ns)] if gran != PT else pool[trial * 4:trial * 4 + 1]
+        sc = sc * rng.uniform(0.9, 1.1, sc.shape).astype(np.float32) if trial == 3 else sc
+        _check(bits, fmt, gran, gs.FP8_SCALE_GIVEN, dev, np.ascontiguousarray(sc, np.float32))
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_every_bf16_x_amax_pair(fmt, dev):
+    """Every pair of positive finite BF16 values x <= amax, laid out as 1x128
+    blocks that each hold one amax and 127 values x (both signs): the codes
+    from the reciprocal-and-FMA division equal the oracle's IEEE division
+    for the whole input space of BF16 x and block amax."""
+    pos = np.arange(1, 0x7F80, dtype=np.uint16)            # positive finite BF16
+    blocks_done = 0
+    chunk_amax = 4096
+    for a0 in range(0, pos.size, chunk_amax):
+        amaxes = pos[a0:a0 + chunk_amax]
+        rows = []
+        for a in amaxes:
+            xs = pos[:np.searchsorted(pos, a, side="right")]
+            nb = -(-xs.size // 127)
+            pad = np.full(nb * 127, a, np.uint16)
+            pad[:xs.size] = xs
+            blk = np.empty((nb, 128), np.uint16)
+            blk[:, 0] = a
+            blk[:, 1:] = pad.reshape(nb, 127)
+            blk[1::2, 1:] |= 0x8000                       # negative copies in odd blocks
+            rows.append(blk)
+        x = np.ascontiguousarray(np.concatenate(rows))
+        c, s, _, _ = _run(x, fmt, B1, gs.FP8_SCALE_FROM_AMAX, dev)
+        rc, rs, _ = oracle.quantize(x, fmt, B1)
+        assert np.array_equal(s, rs.view(np.uint32))
+        if not np.array_equal(c, rc):
+            bad = np.argwhere(c != rc)[:5]
+            raise AssertionError("pair mismatch at %s" % [(hex(x[tuple(b)]), hex(x[b[0], 0]))
+                                                          for b in bad])
+        blocks_done += x.shape[0]
+    assert blocks_done > 4_000_000
+
+
+def test_dequantize_all_codes_all_granularities(dev):
+    rng = np.random.default_rng(5)
+    for fmt in (E4M3, E5M2):
+        for gran, (rows, cols) in ((PT, (16, 16)), (B1, (2, 256)), (B128, (128, 256))):
+            codes = np.tile(np.arange(256, dtype=np.uint8), rows * cols // 256).reshape(rows, cols)
+            ns = oracle.n_scales(rows, cols, gran)
+            for sc in (np.float32([1.0] * ns), rng.uniform(1e-3, 10, ns).astype(np.float32),
+                       np.float32([0.0] * ns), np.float32([np.inf] * ns)):
+                c = torch.from_numpy(codes).to(dev)
+                s = torch.from_numpy(sc).to(dev)
+                out = gs.fp8_dequantize(c, fmt, gran, s)
+                ref = oracle.dequantize(codes, fmt, gran, sc)
+                torch.cuda.synchronize()
+                assert np.array_equal(_u32(out), ref.reshape(-1).view(np.uint32))
+
+
+def test_tiny_per_tensor_case(dev):
+    """1024x1024 BF16 N(0,1) per-tensor E4M3 and its dequantization."""
+    q = synth.tiny_quant()
+    bits = synth.as_u16_numpy(synth.to_bf16_tensor(q.gen(torch.arange(q.rows * q.cols))))
+    _check(bits.reshape(q.rows, q.cols), q.fmt, q.gran, gs.FP8_SCALE_FROM_AMAX, dev)
+
+
+def test_abi_shape_and_alignment_errors(dev):
+    x = torch.zeros(128, 200, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(gs.GSError) as e:
+        gs.fp8_quantize(x, E4M3, B1)
+    assert e.value.status == -3
+    y = torch.zeros(4 * 128 + 1, dtype=torch.bfloat16, device=dev)[1:].view(4, 128)
+    with pytest.raises(gs.GSError) as e:
+        gs.fp8_quantize(y, E4M3, B1)                     # 16-byte alignment required
+    assert e.value.status == -6
