@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the loss-scaling + FP8 hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic, HBM-resident input:
+  1. gs_unscale_check over a Llama-3-8B-shaped FP16 gradient set (291 tensors,
+     8,030,261,248 elements, S = 2^15) -> FP32, one launch;
+  2. gs_update_scale (device-resident state; Inf planted in lm_head on step 2);
+  3. fp8_quantize of DeepSeek-V3-shaped BF16 activations 16384x7168 (1x128,
+     E4M3) and weights 7168x18432 (128x128, E4M3), scales from the block amax;
+  4. fp8_dequantize of both back to FP32.
+value = algorithmic bytes of the step (every input read once, every output
+written once) / wall time per step.  Per-kernel times come from HIP events on
+the launch stream inside the timed region.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
+
+Prints one JSON line.  More than one GPU is not supported (this path is
+measured on one GPU; see the sharding notes in the design document).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for FP8 block quantize and fused unscale+inf-check"
+PEAK_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "unscale_check_llama3_8b_pmc.txt")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "loss_scaling_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(src_hash):
+    """HBM bytes per unscale launch from the committed rocprofv3 --pmc
+    summary, or None when it is missing or was taken on other kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    vals = {}
+    for line in open(PMC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(grad_sample, act_rows, wgt_rows):
+    """The oracle (plain single-threaded C) on a bounded sample of the same
+    workload; inputs are host copies of the device tensors."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    oracle.unscale_check([grad_sample], 32768.0)
+    t_un = time.perf_counter() - t0
+    nbytes = grad_sample.size * 6
+    t0 = time.perf_counter()
+    for x, gran in ((act_rows, 1), (wgt_rows, 2)):
+        codes, scales, _ = oracle.quantize(x, 0, gran)
+        oracle.dequantize(codes, 0, gran, scales)
+        n = x.size
+        nbytes += n * 3 + scales.size * 4 + n * 5 + scales.size * 4
+    t_q = time.perf_counter() - t0
+    del np
+    return {"value": round(nbytes / (t_un + t_q) / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d FP16 elements of the embedding gradient unscaled (%.1f s), "
+                      "%dx%d activation rows 1x128 + %dx%d weight rows 128x128 quantized "
+                      "and dequantized (%.1f s), E4M3; single-threaded C oracle"
+                      % (grad_sample.size, t_un, act_rows.shape[0], act_rows.shape[1],
+                         wgt_rows.shape[0], wgt_rows.shape[1], t_q)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 6 plain copy kernels of 1 GiB (for HBM counter calibration)")
+    ap.add_argument("--pmc-safe", action="store_true",
+                    help="for rocprofv3 --pmc runs: constant inputs (few kernel launches), no "
+                         "device-to-device or device-to-host memcpy, no copy ceiling, no "
+                         "final-state readback, no CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU path only: --gpus must be 1 "
+              "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import loss_scaling_fp8_amd as gs
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # int32 -> float32 converting copy: an elementwise kernel reading and
+        # writing 4 bytes per element (a same-type copy would be a memcpy)
+        a = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+        b = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(6):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": {"read": a.numel() * 4,
+                                                                "write": b.numel() * 4}}))
+        return
+    gs.lib()
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    gset = synth.llama3_8b_gradset()
+    grads, outs = [], []
+    for t, sp in enumerate(gset.tensors):
+        if args.pmc_safe:
+            # counter runs: constant inputs, one fill kernel per tensor (HBM
+            # traffic does not depend on the values)
+            grads.append(torch.empty(sp.numel, dtype=torch.float16, device=dev).fill_(0.5))
+        else:
+            grads.append(gset.full(t, dev))
+        outs.append(torch.empty(sp.numel, dtype=torch.float32, device=dev))
+        if t % 40 == 0:
+            log("generated gradient %d/%d (%.0f s)" % (t + 1, len(gset.tensors), time.time() - t0))
+    act, wgt = synth.deepseek_v3_blocks()
+    if args.pmc_safe:
+        xa = torch.empty((act.rows, act.cols), dtype=torch.bfloat16, device=dev).fill_(0.5)
+        xw = torch.empty((wgt.rows, wgt.cols), dtype=torch.bfloat16, device=dev).fill_(0.5)
+    else:
+        xa, xw = act.full(dev), wgt.full(dev)
+    ca = torch.empty((act.rows, act.cols), dtype=torch.uint8, device=dev)
+    cw = torch.empty((wgt.rows, wgt.cols), dtype=torch.uint8, device=dev)
+    sa = torch.empty(gs.scale_shape(act.rows, act.cols, act.gran), dtype=torch.float32, device=dev)
+    sw = torch.empty(gs.scale_shape(wgt.rows, wgt.cols, wgt.gran), dtype=torch.float32, device=dev)
+    da = torch.empty((act.rows, act.cols), dtype=torch.float32, device=dev)
+    dw = torch.empty((wgt.rows, wgt.cols), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("inputs resident in HBM (%.0f s)" % (time.time() - t0))
+
+    S = torch.empty(1, dtype=torch.float32, device=dev)
+    tracker = torch.empty(1, dtype=torch.int32, device=dev)
+    found = torch.empty(1, dtype=torch.int32, device=dev)
+    skips = torch.empty(1, dtype=torch.int64, device=dev)
+
+    def reset_state():
+        S.fill_(gset.scale)
+        tracker.zero_()
+        found.zero_()
+        skips.zero_()
+
+    inj_t, inj_i, _ = gset.injections[2][0]
+    inj_slot = grads[inj_t][inj_i:inj_i + 1]
+    inj_orig = float(synth.to_f16_tensor(gset.gen(inj_t, torch.tensor([inj_i]))).float()[0])
+
+    n_grad = gset.total
+    n_a, n_w = act.rows * act.cols, wgt.rows * wgt.cols
+    ns_a, ns_w = sa.numel(), sw.numel()
+    bytes_unscale = n_grad * (2 + 4)
+    bytes_qa = n_a * 3 + ns_a * 4
+    bytes_qw = n_w * 3 + ns_w * 4
+    bytes_da = n_a * 5 + ns_a * 4
+    bytes_dw = n_w * 5 + ns_w * 4
+    bytes_update = 4 + 4 + 4 + 8 + 4 + 4 + 4 + 8
+    step_bytes = bytes_unscale + bytes_update + bytes_qa + bytes_qw + bytes_da + bytes_dw
+
+    names = ["unscale_check", "update_scale", "quant_1x128", "quant_128x128",
+             "dequant_1x128", "dequant_128x128"]
+
+    def step(k, ev):
+        if k == 2:
+            inj_slot.fill_(float("inf"))
+        calls = [
+            lambda: gs.gs_unscale_check(grads, outs, S, found),
+            lambda: gs.gs_update_scale(S, tracker, found, 2.0, 0.5, 2000, skips),
+            lambda: gs.fp8_quantize(xa, act.fmt, act.gran, gs.FP8_SCALE_FROM_AMAX, ca, sa),
+            lambda: gs.fp8_quantize(xw, wgt.fmt, wgt.gran, gs.FP8_SCALE_FROM_AMAX, cw, sw),
+            lambda: gs.fp8_dequantize(ca, act.fmt, act.gran, sa, da),
+            lambda: gs.fp8_dequantize(cw, wgt.fmt, wgt.gran, sw, dw),
+        ]
+        for j, c in enumerate(calls):
+            if ev is not None:
+                ev[j][0].record()
+            c()
+            if ev is not None:
+                ev[j][1].record()
+        if k == 2:
+            inj_slot.fill_(inj_orig)
+
+    reset_state()
+    for w in range(args.warmup):
+        step(w + 1, None)
+    torch.cuda.synchronize()
+    log("warmup done")
+    reset_state()
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in names] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(1, args.steps + 1):
+        step(k, events[k - 1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    per_kernel_ms = {n: float(np.mean([events[k][j][0].elapsed_time(events[k][j][1])
+                                       for k in range(args.steps)]))
+                     for j, n in enumerate(names)}
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+    state, copy_gbps = (None, None, None), None
+    if not args.pmc_safe:
+        state = (float(S.item()), int(tracker.item()), int(skips.item()))
+        log("final S=%g tracker=%d skips=%d" % state)
+        # copy ceiling: a plain device copy of 1 GiB (2 GiB moved), outside the step
+        src = outs[0].view(-1)[: 1 << 28]
+        cbuf = torch.empty_like(src)
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cbuf.copy_(src)
+        ce0.record()
+        for _ in range(5):
+            cbuf.copy_(src)
+        ce1.record()
+        torch.cuda.synchronize()
+        copy_gbps = round(5 * 2 * src.numel() * 4 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9, 1)
+
+    kbytes = {"unscale_check": bytes_unscale, "update_scale": bytes_update,
+              "quant_1x128": bytes_qa, "quant_128x128": bytes_qw,
+              "dequant_1x128": bytes_da, "dequant_128x128": bytes_dw}
+    kernels = {}
+    for n in names:
+        gbps = kbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9
+        kernels[n] = {"ms": round(per_kernel_ms[n], 4), "bytes": kbytes[n],
+                      "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
+
+    src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp", "device_fp8.hpp"])
+    un = kernels["unscale_check"]
+    roofline = {"bound": "hbm", "achieved": un["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(un["GBps"] / PEAK_GBPS, 4), "traffic": pmc_traffic(src_hash),
+                "kernel": "unscale_check_kernel", "algorithmic_bytes_per_launch": bytes_unscale}
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b fp16 grad set unscale+check+update (291 tensors, "
+                               "8030261248 elems, S=2^15, Inf in lm_head at step 2) + "
+                               "deepseek-v3 act 16384x7168 1x128 and wgt 7168x18432 128x128 "
+                               "E4M3 quantize+dequantize",
+                   "step_bytes": step_bytes, "grad_elems": n_grad,
+                   "act_shape": [act.rows, act.cols], "wgt_shape": [wgt.rows, wgt.cols]},
+        "roofline": roofline,
+        "kernels": kernels,
+        "copy_ceiling_GBps": copy_gbps,
+        "final_state": {"S": state[0], "tracker": state[1], "skips": state[2]},
+    }
+    if not args.no_cpu_baseline and not args.pmc_safe:
+        log("cpu baseline (oracle) ...")
+        g_host = grads[0].view(-1).cpu().view(torch.int16).numpy().view(np.uint16)
+        a_host = xa[:2048].cpu().view(torch.int16).numpy().view(np.uint16)
+        w_host = xw[:1024].cpu().view(torch.int16).numpy().view(np.uint16)
+        result["cpu_baseline"] = cpu_baseline(g_host, a_host, w_host)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

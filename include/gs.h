@@ -80,8 +80,12 @@ typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
  *              zeroes it once per step, several calls may OR into it, and
  *              gs_update_scale consumes and clears it).
  *   stream     hipStream_t.
- * The device copy of the (pointer, size) list is cached by the library, so a
- * repeated call with the same list uploads nothing.
+ * The list is cut into 2048-element chunks whose descriptors (addresses and
+ * sizes) are built on the first call with a given (grads, outs, numels) list
+ * and cached on the device (at most 64 lists / 1 GiB, least recently used
+ * evicted; an eviction waits for the device), so a repeated call with the
+ * same list uploads nothing.  Device addresses must lie below 2^48
+ * (GS_ERR_ARG otherwise; every current AMD GPU address does).
  */
 gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *outs,
                            const int64_t *numels, gs_dtype in_dtype, const float *scale,

@@ -1,8 +1,9 @@
 // api.hip -- the C ABI of libgsfp8 (declared in include/gs.h): argument
-// validation on the host, the cached device work lists of the multi-tensor
-// unscale, and dispatch to the kernels.  No entry point synchronises the
-// host or reads device memory; the only device allocation happens the first
-// time a given gradient list is seen (its work list is cached).
+// validation on the host, the cached per-chunk descriptors of the
+// multi-tensor unscale, and dispatch to the kernels.  No entry point
+// synchronises the host or reads device memory; the only device allocation
+// happens the first time a given gradient list is seen (its descriptors are
+// cached).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -23,18 +24,21 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 // ------------------------------------------------------------ work-list cache
 // Key: device id + the (input, output, numel) triplets.  Value: one device
-// allocation holding the WorkList arrays.  Least-recently-used eviction; an
-// evicted list may still be referenced by queued kernels, so eviction waits
-// for the device before freeing.
+// allocation holding the per-chunk descriptors.  Least-recently-used
+// eviction by count and by bytes; an evicted list may still be referenced by
+// queued kernels, so eviction waits for the device before freeing.
 struct CachedList {
     void *dev = nullptr;
-    gsk::WorkList wl{};
+    int64_t nchunks = 0;
+    size_t bytes = 0;
 };
 
 constexpr size_t kCacheEntries = 64;
+constexpr size_t kCacheBytes = size_t(1) << 30;
 
 struct ListCache {
     std::mutex mu;
+    size_t bytes = 0;
     std::list<std::string> lru;   // front = most recent
     std::unordered_map<std::string, std::pair<CachedList, std::list<std::string>::iterator>> map;
 };
@@ -62,49 +66,43 @@ std::string make_key(int device, int32_t n, const void *const *in, float *const 
 
 gs_status build_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
                      CachedList &cl) {
-    // layout: chunk_begin[n+1] | in[n] | out[n] | numel[n] | vec_ok[n] (int32)
-    const size_t b_begin = 0;
-    const size_t b_in = b_begin + size_t(n + 1) * 8;
-    const size_t b_out = b_in + size_t(n) * 8;
-    const size_t b_numel = b_out + size_t(n) * 8;
-    const size_t b_vec = b_numel + size_t(n) * 8;
-    const size_t bytes = b_vec + size_t(n) * 4;
-    std::vector<unsigned char> host(bytes);
-    int64_t *begin = reinterpret_cast<int64_t *>(host.data() + b_begin);
-    uint64_t *hin = reinterpret_cast<uint64_t *>(host.data() + b_in);
-    uint64_t *hout = reinterpret_cast<uint64_t *>(host.data() + b_out);
-    int64_t *hnum = reinterpret_cast<int64_t *>(host.data() + b_numel);
-    int32_t *hvec = reinterpret_cast<int32_t *>(host.data() + b_vec);
-    int64_t acc = 0;
+    using gsk::ChunkDesc;
+    using gsk::kUnscaleChunk;
+    int64_t total = 0;
+    for (int32_t i = 0; i < n; ++i) total += (numel[i] + kUnscaleChunk - 1) / kUnscaleChunk;
+    std::vector<ChunkDesc> host(static_cast<size_t>(total));
+    size_t k = 0;
     for (int32_t i = 0; i < n; ++i) {
-        begin[i] = acc;
-        acc += (numel[i] + gsk::kUnscaleChunk - 1) / gsk::kUnscaleChunk;
-        hin[i] = uint64_t(uintptr_t(in[i]));
-        hout[i] = uint64_t(uintptr_t(out[i]));
-        hnum[i] = numel[i];
-        hvec[i] = ((uintptr_t(in[i]) | uintptr_t(out[i])) & 15u) == 0 ? 1 : 0;
+        if (numel[i] == 0) continue;
+        const uint64_t a_in = uint64_t(uintptr_t(in[i]));
+        const uint64_t a_out = uint64_t(uintptr_t(out[i]));
+        const uint64_t last_in = a_in + uint64_t(numel[i]) * 2;
+        const uint64_t last_out = a_out + uint64_t(numel[i]) * 4;
+        if (last_in > gsk::kAddrMask || last_out > gsk::kAddrMask) return GS_ERR_ARG;
+        const uint64_t scalar = ((a_in | a_out) & 15u) ? 1u : 0u;
+        for (int64_t st = 0; st < numel[i]; st += kUnscaleChunk) {
+            const int64_t left = numel[i] - st;
+            const uint64_t ragged = left < kUnscaleChunk ? uint64_t(left) : 0u;
+            host[k].in_bits = (a_in + uint64_t(st) * 2) | (ragged << 48);
+            host[k].out_bits = (a_out + uint64_t(st) * 4) | scalar;
+            ++k;
+        }
     }
-    begin[n] = acc;
+    const size_t bytes = host.size() * sizeof(ChunkDesc);
     void *dev = nullptr;
     if (hipMalloc(&dev, bytes) != hipSuccess) return GS_ERR_HIP;
     if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(dev);
         return GS_ERR_HIP;
     }
-    unsigned char *d = static_cast<unsigned char *>(dev);
     cl.dev = dev;
-    cl.wl.chunk_begin = reinterpret_cast<const int64_t *>(d + b_begin);
-    cl.wl.in = reinterpret_cast<const uint16_t *const *>(d + b_in);
-    cl.wl.out = reinterpret_cast<float *const *>(d + b_out);
-    cl.wl.numel = reinterpret_cast<const int64_t *>(d + b_numel);
-    cl.wl.vec_ok = reinterpret_cast<const int32_t *>(d + b_vec);
-    cl.wl.n = n;
-    cl.wl.total_chunks = acc;
+    cl.nchunks = total;
+    cl.bytes = bytes;
     return GS_OK;
 }
 
 gs_status get_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
-                   gsk::WorkList &wl) {
+                   CachedList &result) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return GS_ERR_HIP;
     std::string key = make_key(device, n, in, out, numel);
@@ -113,23 +111,24 @@ gs_status get_list(int32_t n, const void *const *in, float *const *out, const in
     auto it = c.map.find(key);
     if (it != c.map.end()) {
         c.lru.splice(c.lru.begin(), c.lru, it->second.second);
-        wl = it->second.first.wl;
+        result = it->second.first;
         return GS_OK;
     }
     CachedList cl;
     const gs_status st = build_list(n, in, out, numel, cl);
     if (st != GS_OK) return st;
-    if (c.map.size() >= kCacheEntries) {
-        const std::string &old = c.lru.back();
-        auto oit = c.map.find(old);
+    while (!c.lru.empty() && (c.map.size() >= kCacheEntries || c.bytes + cl.bytes > kCacheBytes)) {
+        auto oit = c.map.find(c.lru.back());
         (void)hipDeviceSynchronize();        // queued kernels may still read it
         (void)hipFree(oit->second.first.dev);
+        c.bytes -= oit->second.first.bytes;
         c.map.erase(oit);
         c.lru.pop_back();
     }
     c.lru.push_front(key);
     c.map.emplace(key, std::make_pair(cl, c.lru.begin()));
-    wl = cl.wl;
+    c.bytes += cl.bytes;
+    result = cl;
     return GS_OK;
 }
 
@@ -178,10 +177,11 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
         if (total > kMaxElems * 64) return GS_ERR_SIZE;
     }
     if (total == 0) return GS_OK;
-    gsk::WorkList wl;
-    const gs_status st = get_list(n, grads, outs, numels, wl);
+    CachedList cl;
+    const gs_status st = get_list(n, grads, outs, numels, cl);
     if (st != GS_OK) return st;
-    return from_hip(gsk::launch_unscale_check(wl, scale, found_inf,
+    return from_hip(gsk::launch_unscale_check(static_cast<const gsk::ChunkDesc *>(cl.dev),
+                                              cl.nchunks, scale, found_inf,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -11,27 +11,28 @@
 namespace gsk {
 
 // ---------------------------------------------------------------- unscale
-// Device view of a cached multi-tensor work list.  Every tensor is cut into
-// chunks of kUnscaleChunk elements (the last one ragged); chunk_begin is the
-// prefix sum of the chunk counts, so a flat chunk id maps to its tensor by a
-// binary search over n+1 entries.
-struct WorkList {
-    const int64_t *chunk_begin;   // [n + 1]
-    const uint16_t *const *in;    // [n] FP16 gradients
-    float *const *out;            // [n] FP32 outputs
-    const int64_t *numel;         // [n]
-    const int32_t *vec_ok;        // [n] 1 when both bases are 16-byte aligned
-    int32_t n;
-    int64_t total_chunks;
+// The gradient list is cut into chunks of kUnscaleChunk elements (the last
+// chunk of a tensor ragged), and each chunk gets a 16-byte descriptor built
+// once on the host and cached on the device:
+//   in_bits  = address of the chunk's first FP16 element (bits 0..47)
+//              | element count << 48 when the chunk is ragged (else 0)
+//   out_bits = address of the chunk's first FP32 output
+//              | 1 when the tensor is not 16-byte aligned (element-wise path)
+// One workgroup per chunk needs a single dependent (scalar) load before it
+// streams its data.
+struct ChunkDesc {
+    uint64_t in_bits;
+    uint64_t out_bits;
 };
 
 constexpr int kUnscaleThreads = 256;
-constexpr int kUnscaleVec = 8;        // FP16 elements per 16-byte load
-constexpr int kUnscaleUnroll = 4;     // loads in flight per lane per chunk
+constexpr int kUnscaleVec = 4;        // FP16 elements per 8-byte load (one 16-byte store)
+constexpr int kUnscaleUnroll = 2;     // loads per lane per chunk
 constexpr int64_t kUnscaleChunk = int64_t(kUnscaleThreads) * kUnscaleVec * kUnscaleUnroll;
+constexpr uint64_t kAddrMask = (uint64_t(1) << 48) - 1;
 
-hipError_t launch_unscale_check(const WorkList &wl, const float *scale, int32_t *found_inf,
-                                hipStream_t stream);
+hipError_t launch_unscale_check(const ChunkDesc *descs, int64_t nchunks, const float *scale,
+                                int32_t *found_inf, hipStream_t stream);
 hipError_t launch_update_scale(float *scale, int32_t *tracker, int32_t *found_inf, float growth,
                                float backoff, int32_t interval, int64_t *skips,
                                hipStream_t stream);

@@ -173,10 +173,13 @@ class GradSet:
     def full(self, t: int, device) -> torch.Tensor:
         n = self.tensors[t].numel
         out = torch.empty(n, dtype=torch.float16, device=device)
+        bits16 = out.view(torch.int16)
         step = 1 << 27
         for lo in range(0, n, step):
             idx = torch.arange(lo, min(n, lo + step), dtype=torch.int64, device=device)
-            out[lo:lo + idx.numel()] = to_f16_tensor(self.gen(t, idx))
+            # an int64 -> int16 converting copy keeps the low 16 bits (an
+            # elementwise kernel, not a device-to-device memcpy)
+            bits16[lo:lo + idx.numel()].copy_(self.gen(t, idx))
         return out
 
     @property
@@ -262,10 +265,11 @@ class QuantSpec:
     def full(self, device) -> torch.Tensor:
         n = self.rows * self.cols
         out = torch.empty(n, dtype=torch.bfloat16, device=device)
+        bits16 = out.view(torch.int16)
         step = 1 << 27
         for lo in range(0, n, step):
             idx = torch.arange(lo, min(n, lo + step), dtype=torch.int64, device=device)
-            out[lo:lo + idx.numel()] = to_bf16_tensor(self.gen(idx))
+            bits16[lo:lo + idx.numel()].copy_(self.gen(idx))
         return out.view(self.rows, self.cols)
 
 
