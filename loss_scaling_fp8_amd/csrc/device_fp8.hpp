@@ -22,55 +22,46 @@ template <int FMT> struct Fp8;
 template <> struct Fp8<0> {                           // OCP E4M3
     static constexpr uint32_t kMaxBits = 0x43E00000u;       // 448.0f
     static constexpr float kMax = 448.0f;
-    static constexpr uint32_t kMinNormalBits = 0x3C800000u; // 2^-6
-    static constexpr int kDrop = 20;                        // 23 - 3 fraction bits
-    static constexpr uint32_t kRebias = (127u - 7u) << 23;  // FP32 -> FP8 exponent
-    static constexpr float kSubAnchor = 16384.0f;           // 2^14, FP32 ulp 2^-9
 };
 
 template <> struct Fp8<1> {                           // OCP E5M2
     static constexpr uint32_t kMaxBits = 0x47600000u;       // 57344.0f
     static constexpr float kMax = 57344.0f;
-    static constexpr uint32_t kMinNormalBits = 0x38800000u; // 2^-14
-    static constexpr int kDrop = 21;                        // 23 - 2 fraction bits
-    static constexpr uint32_t kRebias = (127u - 15u) << 23;
-    static constexpr float kSubAnchor = 128.0f;             // 2^7, FP32 ulp 2^-16
 };
 
 __device__ __forceinline__ float as_f32(uint32_t b) { return __uint_as_float(b); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
 
-// FP8 magnitude code (0 .. max code) of a non-negative, non-NaN FP32 value
-// given by its bits `b` (Inf and anything above MAX saturate).
-//  - Normal FP8 range: drop the extra FP32 fraction bits with
-//    round-to-nearest-even; a carry out of the fraction lands in the
-//    exponent field, which is exactly the next FP8 code.
-//  - Below the smallest FP8 normal: adding an anchor whose FP32 ulp equals
-//    the FP8 subnormal spacing makes the FP32 adder itself round the value
-//    to that spacing (ties to even); the difference of the bit patterns is
-//    the subnormal code (the top value is the smallest normal's code).
+// Round-to-nearest-even FP32 -> FP8 by gfx950's OCP conversion, two values
+// per instruction, into the low (HI = false) or high 16 bits of `old`.
+// Black-box checked over all 2^32 FP32 inputs of both formats: for every
+// non-NaN input within [-MAX, MAX] it returns exactly the code of the
+// format definition (subnormals, ties to even, the sign of zero); values
+// above MAX but below the next would-be FP8 value's midpoint (E4M3: 464,
+// E5M2: 61440) also give the MAX code.  NaN inputs are never passed (their
+// sign and payload rules differ), nor larger magnitudes (they give NaN/Inf).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
+    if constexpr (FMT == 0)
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+    else
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
+}
+
 template <int FMT>
-__device__ __forceinline__ uint32_t encode_mag(uint32_t b) {
-    using T = Fp8<FMT>;
-    b = b < T::kMaxBits ? b : T::kMaxBits;
-    const uint32_t lsb = (b >> T::kDrop) & 1u;
-    const uint32_t normal =
-        (b - T::kRebias + ((1u << (T::kDrop - 1)) - 1u) + lsb) >> T::kDrop;
-    const uint32_t sub = as_u32(as_f32(b) + T::kSubAnchor) - as_u32(T::kSubAnchor);
-    return b < T::kMinNormalBits ? sub : normal;
+__device__ __forceinline__ float clamp_max(float y) {     // y not NaN
+    return __builtin_fabsf(y) > Fp8<FMT>::kMax ? __builtin_copysignf(Fp8<FMT>::kMax, y) : y;
 }
 
 // Full code of x / s for any FP32 x and s (IEEE division), following the
 // cast definition: NaN x -> sign|0x7F; NaN quotient -> 0x7F; otherwise the
-// sign of the quotient with the saturated, rounded magnitude.
+// quotient clamped to [-MAX, MAX] and rounded to nearest even (sign kept).
 template <int FMT>
 __device__ __forceinline__ uint32_t cast_exact(float x, float s) {
-    const uint32_t xb = as_u32(x);
-    if (__builtin_isnan(x)) return ((xb >> 24) & 0x80u) | 0x7Fu;
+    if (__builtin_isnan(x)) return ((as_u32(x) >> 24) & 0x80u) | 0x7Fu;
     const float y = x / s;
     if (__builtin_isnan(y)) return 0x7Fu;
-    const uint32_t yb = as_u32(y);
-    return ((yb >> 24) & 0x80u) | encode_mag<FMT>(yb & 0x7FFFFFFFu);
+    return cvt_pk<FMT, false>(clamp_max<FMT>(y), 0.0f, 0u) & 0xFFu;
 }
 
 // |x| / s for finite |x| >= 0 and s in the "fast" range [2^-80, 2^126],
@@ -92,25 +83,23 @@ __device__ __forceinline__ bool fast_scale(float s) {
     return (as_u32(s) - 0x17800000u) <= (0x7E800000u - 0x17800000u);
 }
 
-// Exact FP32 value of an FP8 code.
-template <int FMT> __device__ __forceinline__ float decode(uint32_t c);
+// Exact FP32 values of the four FP8 codes packed in a 32-bit word (byte 0
+// first), by gfx950's OCP FP8 -> FP32 conversion.  Every non-NaN code
+// converts exactly (checked for all 256 codes of both formats against the
+// format definition); NaN codes give a NaN, which callers canonicalise.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-template <> __device__ __forceinline__ float decode<0>(uint32_t c) {
-    const uint32_t m = c & 0x7Fu;
-    const uint32_t sign = (c & 0x80u) << 24;
-    // subnormals (exponent field 0): m * 2^-9; normals: rebias the exponent
-    const float sub = (float)m * 0x1p-9f;
-    const uint32_t mag = m < 8u ? as_u32(sub) : (m << 20) + Fp8<0>::kRebias;
-    const uint32_t bits = (m == 0x7Fu) ? 0x7FC00000u : (mag | sign);
-    return as_f32(bits);
-}
-
-template <> __device__ __forceinline__ float decode<1>(uint32_t c) {
-    // E5M2 has FP16's sign, exponent width and bias: it is the upper byte of
-    // an FP16 encoding, and FP16 -> FP32 widening is exact (subnormals,
-    // infinities and NaNs included).
-    const _Float16 h = __builtin_bit_cast(_Float16, (unsigned short)((c & 0xFFu) << 8));
-    return (float)h;
+template <int FMT>
+__device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
+    f32x2_t lo, hi;
+    if constexpr (FMT == 0) {
+        lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    } else {
+        lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+    }
+    v[0] = lo.x; v[1] = lo.y; v[2] = hi.x; v[3] = hi.y;
 }
 
 // FP32 result written for a dequantized value: canonical NaN for any NaN.

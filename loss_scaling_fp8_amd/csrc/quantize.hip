@@ -30,9 +30,37 @@
 #include "device_fp8.hpp"
 #include "gs_internal.hpp"
 
+#ifndef GS_QUANT_NT_LOAD
+#define GS_QUANT_NT_LOAD 1
+#endif
+#ifndef GS_QUANT_NT_STORE
+#define GS_QUANT_NT_STORE 1
+#endif
+
 namespace gsk {
 
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+#if GS_QUANT_NT_LOAD
+    return __builtin_nontemporal_load(q);
+#else
+    return *q;
+#endif
+}
+
+template <typename V>
+__device__ __forceinline__ void st(void *p, V v) {
+#if GS_QUANT_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
+#else
+    *reinterpret_cast<V *>(p) = v;
+#endif
+}
 
 constexpr uint32_t kFloorBits = 0x2B8CBCCCu;  // fl32(1e-12)
 
@@ -53,10 +81,9 @@ struct LaneData {
     uint32_t w[kWords];
 
     __device__ __forceinline__ void load(const IN *p) {
-        const uint4 *v = reinterpret_cast<const uint4 *>(p);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const uint4 t = v[i];
+            const u32x4 t = ld16(p + i * kPerVec);
             w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
         }
     }
@@ -64,7 +91,7 @@ struct LaneData {
     __device__ __forceinline__ void load_strided(const IN *p, int64_t stride) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const uint4 t = *reinterpret_cast<const uint4 *>(p + i * stride);
+            const u32x4 t = ld16(p + i * stride);
             w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
         }
     }
@@ -118,22 +145,26 @@ struct LaneData {
     }
 
     // FP8 codes of all lane elements, 4 per output word (little-endian).
-    template <int FMT>
+    // Fast path (finite lane, scale in the fast range): |x| / s by the
+    // reciprocal and one FMA correction, the sign of x put back, and the
+    // hardware conversion; a clamp only when the scale was given (with a
+    // scale from this block's amax, |x / s| <= MAX (1 + 2^-23)).
+    template <int FMT, bool CLAMP>
     __device__ __forceinline__ void cast(float s, bool lane_nonfinite,
                                          uint32_t (&out)[kElems / 4]) const {
         const float r = 1.0f / s;
         if (fast_scale(s) && !lane_nonfinite) {
 #pragma unroll
             for (int j = 0; j < kElems / 4; ++j) {
-                uint32_t acc = 0;
+                float q[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const uint32_t e = elem(4 * j + k);
-                    const float q = div_by_scale(as_f32(e & 0x7FFFFFFFu), s, r);
-                    const uint32_t c = encode_mag<FMT>(as_u32(q)) | ((e >> 24) & 0x80u);
-                    acc |= c << (8 * k);
+                    float a = div_by_scale(__builtin_fabsf(as_f32(e)), s, r);
+                    if (CLAMP) a = as_f32(min(as_u32(a), Fp8<FMT>::kMaxBits));
+                    q[k] = as_f32(as_u32(a) | (e & 0x80000000u));
                 }
-                out[j] = acc;
+                out[j] = cvt_pk<FMT, true>(q[2], q[3], cvt_pk<FMT, false>(q[0], q[1], 0u));
             }
         } else {
 #pragma unroll
@@ -151,11 +182,9 @@ struct LaneData {
 __device__ __forceinline__ void store_words(uint8_t *p, const uint32_t *w, int nwords) {
     // nwords is a compile-time multiple of 1..4 words; 16-byte pieces first
     int i = 0;
-    for (; i + 4 <= nwords; i += 4)
-        *reinterpret_cast<uint4 *>(p + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
-    for (; i + 2 <= nwords; i += 2)
-        *reinterpret_cast<uint2 *>(p + 4 * i) = make_uint2(w[i], w[i + 1]);
-    for (; i < nwords; ++i) *reinterpret_cast<uint32_t *>(p + 4 * i) = w[i];
+    for (; i + 4 <= nwords; i += 4) st(p + 4 * i, u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]});
+    for (; i + 2 <= nwords; i += 2) st(p + 4 * i, u32x2{w[i], w[i + 1]});
+    for (; i < nwords; ++i) st(p + 4 * i, w[i]);
 }
 
 // ---------------------------------------------------------------- 1x128
@@ -186,7 +215,7 @@ void quant_1x128_kernel(const IN *__restrict__ x, int64_t nblocks, uint8_t *__re
             s = scales[b];
         }
         uint32_t out[kElems / 4];
-        L.template cast<FMT>(s, nf, out);
+        L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
         store_words(codes + b * 128 + sub * kElems, out, kElems / 4);
     }
     if (saw_nf && nonfinite) *nonfinite = 1;
@@ -230,16 +259,16 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
             s = scales[t];
         }
         uint32_t out[LaneData<IN, kPasses>::kElems / 4];
-        L.template cast<FMT>(s, nf, out);
+        L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
         // each pass contributes kPerVec codes of one row
         constexpr int kWordsPerPass = kPerVec / 4;
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
             uint8_t *dst = codes + base + int64_t(p) * kRowsPerPass * cols;
             if constexpr (kWordsPerPass == 2)
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(out[2 * p], out[2 * p + 1]);
+                st(dst, u32x2{out[2 * p], out[2 * p + 1]});
             else
-                *reinterpret_cast<uint32_t *>(dst) = out[p];
+                st(dst, out[p]);
         }
     }
     if (saw_nf && nonfinite) *nonfinite = 1;
@@ -317,7 +346,7 @@ void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, const uint32_t *__
         const bool nf = L.absmax(a);
         saw_nf |= nf;
         uint32_t out[kPerVec / 4];
-        L.template cast<FMT>(s, nf, out);
+        L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
         store_words(codes + v * kPerVec, out, kPerVec / 4);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
@@ -332,58 +361,78 @@ void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, const uint32_t *__
 }
 
 // ---------------------------------------------------------------- dequantize
-// 16 codes per lane-step -> 16 FP32 (4 x 16-byte stores).
+// Each lane turns 4 codes (one 4-byte load) into 4 FP32 (one 16-byte
+// non-temporal store), so every wave-wide store instruction writes 1 KiB of
+// contiguous output; a lane handles 4 such groups per work item.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int FMT>
-__device__ __forceinline__ void dequant16(uint4 c, float s, float4 *dst) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float v[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v[b] = canon(decode<FMT>((w[k] >> (8 * b)) & 0xFFu) * s);
-        dst[k] = make_float4(v[0], v[1], v[2], v[3]);
-    }
+__device__ __forceinline__ void dequant_group(uint32_t w, float s, f32x4 *dst) {
+    float v[4];
+    decode4<FMT>(w, v);
+    const f32x4 o = {canon(v[0] * s), canon(v[1] * s), canon(v[2] * s), canon(v[3] * s)};
+    __builtin_nontemporal_store(o, dst);
 }
 
-// per-tensor (BLOCKED = false) or 1x128 (BLOCKED = true): flat walk
+template <int FMT>
+__device__ __forceinline__ float dequant_one(uint8_t c, float s) {
+    float v[4];
+    decode4<FMT>(c, v);
+    return canon(v[0] * s);
+}
+
+// per-tensor (BLOCKED = false) or 1x128 (BLOCKED = true): flat walk over
+// groups of 4 codes; a 128-code block is 32 consecutive groups.
 template <int FMT, bool BLOCKED>
 __global__ __launch_bounds__(256)
 void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
                            const float *__restrict__ scales, float *__restrict__ out) {
-    const int64_t nvec = n / 16;
+    constexpr int U = 4;
+    const int64_t ngroups = n / 4;
     const float s0 = BLOCKED ? 0.0f : scales[0];
-    for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec;
-         v += int64_t(gridDim.x) * 256) {
-        const uint4 c = reinterpret_cast<const uint4 *>(codes)[v];
-        const float s = BLOCKED ? scales[v >> 3] : s0;       // 8 vectors per 128-block
-        dequant16<FMT>(c, s, reinterpret_cast<float4 *>(out + v * 16));
+    const uint32_t *cw = reinterpret_cast<const uint32_t *>(codes);
+    f32x4 *o4 = reinterpret_cast<f32x4 *>(out);
+    for (int64_t g0 = int64_t(blockIdx.x) * 256 * U; g0 < ngroups;
+         g0 += int64_t(gridDim.x) * 256 * U) {
+        uint32_t w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + u * 256 + threadIdx.x;
+            w[u] = g < ngroups ? cw[g] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + u * 256 + threadIdx.x;
+            if (g < ngroups) dequant_group<FMT>(w[u], BLOCKED ? scales[g >> 5] : s0, o4 + g);
+        }
     }
-    if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - nvec * 16) {
-        const int64_t i = nvec * 16 + threadIdx.x;
-        out[i] = canon(decode<FMT>(codes[i]) * s0);
+    if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - ngroups * 4) {
+        const int64_t i = ngroups * 4 + threadIdx.x;
+        out[i] = dequant_one<FMT>(codes[i], s0);
     }
 }
 
-// 128x128: one workgroup per tile; 8 lanes per row (16 codes each),
-// 32 rows per pass, 4 passes.
+// 128x128: a work item is a 32-row slab of one tile (4 per tile); 32 lanes
+// per 128-code row, 8 rows per pass, 4 passes.
 template <int FMT>
 __global__ __launch_bounds__(256)
 void dequant_128x128_kernel(const uint8_t *__restrict__ codes, int64_t cols,
-                            int64_t tiles_per_row, int64_t ntiles,
+                            int64_t tiles_per_row, int64_t nitems,
                             const float *__restrict__ scales, float *__restrict__ out) {
-    const int row0 = threadIdx.x >> 3, seg = threadIdx.x & 7;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int r_in = threadIdx.x >> 5;
+    const int c4 = (threadIdx.x & 31) * 4;
+    for (int64_t wi = blockIdx.x; wi < nitems; wi += gridDim.x) {
+        const int64_t t = wi >> 2, slab = wi & 3;
         const int64_t ti = t / tiles_per_row, tj = t - ti * tiles_per_row;
         const float s = scales[t];
-        uint4 c[4];
+        const int64_t base = (ti * 128 + slab * 32 + r_in) * cols + tj * 128 + c4;
+        uint32_t w[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            c[p] = *reinterpret_cast<const uint4 *>(
-                codes + (ti * 128 + row0 + 32 * p) * cols + tj * 128 + seg * 16);
+            w[p] = *reinterpret_cast<const uint32_t *>(codes + base + int64_t(p) * 8 * cols);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            dequant16<FMT>(c[p], s, reinterpret_cast<float4 *>(
-                out + (ti * 128 + row0 + 32 * p) * cols + tj * 128 + seg * 16));
+            dequant_group<FMT>(w[p], s, reinterpret_cast<f32x4 *>(out + base + int64_t(p) * 8 * cols));
     }
 }
 
@@ -439,18 +488,18 @@ hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int 
                           const float *scales, float *out, hipStream_t stream) {
     const int64_t n = rows * cols;
     if (gran == FP8_BLOCK_128x128) {
-        const int64_t tpr = cols / 128, ntiles = (rows / 128) * tpr;
-        if (ntiles == 0) return hipSuccess;
-        hipLaunchKernelGGL((dequant_128x128_kernel<FMT>), dim3(grid_for(ntiles, 1)), dim3(256),
-                           0, stream, codes, cols, tpr, ntiles, scales, out);
+        const int64_t tpr = cols / 128, nitems = (rows / 128) * tpr * 4;
+        if (nitems == 0) return hipSuccess;
+        hipLaunchKernelGGL((dequant_128x128_kernel<FMT>), dim3(grid_for(nitems, 1)), dim3(256),
+                           0, stream, codes, cols, tpr, nitems, scales, out);
         return hipGetLastError();
     }
     if (n == 0) return hipSuccess;
     if (gran == FP8_BLOCK_1x128)
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, true>), dim3(grid_for(n / 16, 256 * 4)),
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, true>), dim3(grid_for(n / 4, 256 * 4)),
                            dim3(256), 0, stream, codes, n, scales, out);
     else
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, false>), dim3(grid_for(n / 16, 256 * 4)),
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, false>), dim3(grid_for(n / 4, 256 * 4)),
                            dim3(256), 0, stream, codes, n, scales, out);
     return hipGetLastError();
 }

@@ -180,3 +180,23 @@ def test_abi_shape_and_alignment_errors(dev):
     with pytest.raises(gs.GSError) as e:
         gs.fp8_quantize(y, E4M3, B1)                     # 16-byte alignment required
     assert e.value.status == -6
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_every_fp32_value_given_scale_one(fmt, dev):
+    """All 2^32 FP32 bit patterns through the per-tensor given-scale cast with
+    s = 1 (y = x exactly): the codes equal the oracle's for the whole FP32
+    input space, NaN, Inf, subnormals and saturation included."""
+    chunk = 1 << 28
+    sc = torch.ones(1, dtype=torch.float32, device=dev)
+    codes = torch.empty((1, chunk), dtype=torch.uint8, device=dev)
+    for lo in range(0, 1 << 32, chunk):
+        host = np.arange(lo, lo + chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        x = torch.from_numpy(host).to(dev).view(1, chunk)
+        gs.fp8_quantize(x, fmt, PT, gs.FP8_SCALE_GIVEN, codes=codes, scales=sc)
+        got = codes.cpu().numpy().reshape(-1)
+        ref = oracle.cast(host, 1.0, fmt)
+        if not np.array_equal(got, ref):
+            bad = np.flatnonzero(got != ref)[:5]
+            raise AssertionError("fp32 patterns %s: gpu %s oracle %s" % (
+                [hex(lo + int(i)) for i in bad], got[bad].tolist(), ref[bad].tolist()))
