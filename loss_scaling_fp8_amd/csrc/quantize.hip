@@ -30,11 +30,24 @@
 #include "device_fp8.hpp"
 #include "gs_internal.hpp"
 
-#ifndef GS_QUANT_NT_LOAD
-#define GS_QUANT_NT_LOAD 1
+// Cache policy per kernel (1 = non-temporal), chosen by measurement.
+#ifndef GS_Q1_NT_LOAD
+#define GS_Q1_NT_LOAD 0
 #endif
-#ifndef GS_QUANT_NT_STORE
-#define GS_QUANT_NT_STORE 1
+#ifndef GS_Q1_NT_STORE
+#define GS_Q1_NT_STORE 0
+#endif
+#ifndef GS_Q128_NT_LOAD
+#define GS_Q128_NT_LOAD 1
+#endif
+#ifndef GS_Q128_NT_STORE
+#define GS_Q128_NT_STORE 0
+#endif
+#ifndef GS_QT_NT_LOAD
+#define GS_QT_NT_LOAD 0
+#endif
+#ifndef GS_QT_NT_STORE
+#define GS_QT_NT_STORE 0
 #endif
 
 namespace gsk {
@@ -44,22 +57,17 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const void *p) {
     const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
-#if GS_QUANT_NT_LOAD
-    return __builtin_nontemporal_load(q);
-#else
-    return *q;
-#endif
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
 }
 
-template <typename V>
+template <bool NT, typename V>
 __device__ __forceinline__ void st(void *p, V v) {
-#if GS_QUANT_NT_STORE
-    __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
-#else
-    *reinterpret_cast<V *>(p) = v;
-#endif
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
+    else *reinterpret_cast<V *>(p) = v;
 }
 
 constexpr uint32_t kFloorBits = 0x2B8CBCCCu;  // fl32(1e-12)
@@ -80,18 +88,20 @@ struct LaneData {
     static constexpr int kWords = NV * 4;
     uint32_t w[kWords];
 
+    template <bool NT>
     __device__ __forceinline__ void load(const IN *p) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const u32x4 t = ld16(p + i * kPerVec);
+            const u32x4 t = ld16<NT>(p + i * kPerVec);
             w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
         }
     }
     // load NV vectors spaced `stride` elements apart
+    template <bool NT>
     __device__ __forceinline__ void load_strided(const IN *p, int64_t stride) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const u32x4 t = ld16(p + i * stride);
+            const u32x4 t = ld16<NT>(p + i * stride);
             w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
         }
     }
@@ -179,12 +189,13 @@ struct LaneData {
     }
 };
 
+template <bool NT>
 __device__ __forceinline__ void store_words(uint8_t *p, const uint32_t *w, int nwords) {
     // nwords is a compile-time multiple of 1..4 words; 16-byte pieces first
     int i = 0;
-    for (; i + 4 <= nwords; i += 4) st(p + 4 * i, u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]});
-    for (; i + 2 <= nwords; i += 2) st(p + 4 * i, u32x2{w[i], w[i + 1]});
-    for (; i < nwords; ++i) st(p + 4 * i, w[i]);
+    for (; i + 4 <= nwords; i += 4) st<NT>(p + 4 * i, u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]});
+    for (; i + 2 <= nwords; i += 2) st<NT>(p + 4 * i, u32x2{w[i], w[i + 1]});
+    for (; i < nwords; ++i) st<NT>(p + 4 * i, w[i]);
 }
 
 // ---------------------------------------------------------------- 1x128
@@ -202,7 +213,7 @@ void quant_1x128_kernel(const IN *__restrict__ x, int64_t nblocks, uint8_t *__re
     for (int64_t b = int64_t(blockIdx.x) * kBlocksPerWG + (threadIdx.x / kLanesPerBlock);
          b < nblocks; b += int64_t(gridDim.x) * kBlocksPerWG) {
         LaneData<IN, NV> L;
-        L.load(x + b * 128 + sub * kElems);
+        L.template load<GS_Q1_NT_LOAD>(x + b * 128 + sub * kElems);
         uint32_t amax_bits;
         const bool nf = L.absmax(amax_bits);
         saw_nf |= nf;
@@ -216,7 +227,7 @@ void quant_1x128_kernel(const IN *__restrict__ x, int64_t nblocks, uint8_t *__re
         }
         uint32_t out[kElems / 4];
         L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
-        store_words(codes + b * 128 + sub * kElems, out, kElems / 4);
+        store_words<GS_Q1_NT_STORE>(codes + b * 128 + sub * kElems, out, kElems / 4);
     }
     if (saw_nf && nonfinite) *nonfinite = 1;
 }
@@ -242,7 +253,7 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
         const int64_t ti = t / tiles_per_row, tj = t - ti * tiles_per_row;
         const int64_t base = (ti * 128 + row0) * cols + tj * 128 + seg * kPerVec;
         LaneData<IN, kPasses> L;
-        L.load_strided(x + base, int64_t(kRowsPerPass) * cols);
+        L.template load_strided<GS_Q128_NT_LOAD>(x + base, int64_t(kRowsPerPass) * cols);
         uint32_t amax_bits;
         const bool nf = L.absmax(amax_bits);
         saw_nf |= nf;
@@ -266,9 +277,9 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
         for (int p = 0; p < kPasses; ++p) {
             uint8_t *dst = codes + base + int64_t(p) * kRowsPerPass * cols;
             if constexpr (kWordsPerPass == 2)
-                st(dst, u32x2{out[2 * p], out[2 * p + 1]});
+                st<GS_Q128_NT_STORE>(dst, u32x2{out[2 * p], out[2 * p + 1]});
             else
-                st(dst, out[p]);
+                st<GS_Q128_NT_STORE>(dst, out[p]);
         }
     }
     if (saw_nf && nonfinite) *nonfinite = 1;
@@ -291,7 +302,7 @@ void amax_partials_kernel(const IN *__restrict__ x, int64_t n, uint32_t *__restr
         LaneData<IN, 1> L[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (v + u * step < nvec) L[u].load(x + (v + u * step) * kPerVec);
+            if (v + u * step < nvec) L[u].template load<GS_QT_NT_LOAD>(x + (v + u * step) * kPerVec);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
             if (v + u * step < nvec) {
@@ -341,13 +352,13 @@ void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, const uint32_t *__
     for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec;
          v += int64_t(gridDim.x) * 256) {
         LaneData<IN, 1> L;
-        L.load(x + v * kPerVec);
+        L.template load<GS_QT_NT_LOAD>(x + v * kPerVec);
         uint32_t a;
         const bool nf = L.absmax(a);
         saw_nf |= nf;
         uint32_t out[kPerVec / 4];
         L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
-        store_words(codes + v * kPerVec, out, kPerVec / 4);
+        store_words<GS_QT_NT_STORE>(codes + v * kPerVec, out, kPerVec / 4);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
         const int64_t i = nvec * kPerVec + threadIdx.x;
