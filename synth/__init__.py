@@ -291,3 +291,129 @@ def deepseek_v3_blocks() -> list:
     0.01% of entries x500 in both."""
     return [QuantSpec("act_1x128", 16384, 7168, 0, 1, 3003, 400, "gauss", 1.0, 1e-4, 500.0),
             QuantSpec("wgt_128x128", 7168, 18432, 0, 2, 3003, 401, "gauss", 0.02, 1e-4, 500.0)]
+
+
+# ------------------------------------------------------------------ special values
+def _bf16_from_f32_bits(b32: torch.Tensor) -> torch.Tensor:
+    return ((b32 + 0x7FFF + ((b32 >> 16) & 1)) >> 16) & 0xFFFF
+
+
+def special_mix_bits(seed: int, stream: int, idx: torch.Tensor) -> torch.Tensor:
+    """BF16 bit patterns, class chosen per element by a hash:
+    90% N(0,1) (Irwin-Hall); 2% NaN (random sign and payload); 2% +-Inf;
+    2% magnitudes 2^U(-24,-14) (FP16-subnormal range); 2% +-0; 1% just above
+    the FP8 maxima (BF16 values 450..480 and 57600..61440); 1% exact
+    E4M3/E5M2 midpoints at scale 1 (a BF16 whose fraction is an FP8 fraction
+    plus one half unit)."""
+    cls = hash_u32(seed, stream, idx, 11) % 100
+    u = hash_u32(seed, stream, idx, 12)
+    sign = (u >> 31) << 15
+    g = bf16_bits(gaussian_f32(seed, stream, idx, 1.0))
+    nan = sign | 0x7F80 | (1 + (u % 127))
+    inf = sign | 0x7F80
+    # log-uniform over [2^-24, 2^-14): BF16 exponent field 103..112
+    tiny = sign | ((103 + (u >> 8) % 10) << 7) | (u & 0x7F)
+    zero = sign
+    # just above 448 (0x43E0) or 57344 (0x4760): BF16 neighbours 1..16 ulps up
+    above = sign | torch.where(((u >> 9) & 1) == 1, 0x43E0 + 1 + (u & 0xF), 0x4760 + 1 + (u & 0xF))
+    # midpoints: E4M3 (fraction bit 3 set below 3 FP8 fraction bits) in the
+    # E4M3 normal range, or E5M2 (bit 4 below 2 fraction bits) in its range
+    e4 = ((121 + (u >> 4) % 15) << 7) | (((u >> 1) & 7) << 4) | 0x8
+    e5 = ((113 + (u >> 4) % 30) << 7) | (((u >> 1) & 3) << 5) | 0x10
+    mid = sign | torch.where((u & 1) == 1, e4, e5)
+    out = g
+    out = torch.where(cls >= 90, nan, out)
+    out = torch.where(cls >= 92, inf, out)
+    out = torch.where(cls >= 94, tiny, out)
+    out = torch.where(cls >= 96, zero, out)
+    out = torch.where(cls >= 98, above, out)
+    out = torch.where(cls >= 99, mid, out)
+    return out
+
+
+def anchored_bits(seed: int, stream: int, idx: torch.Tensor, anchor: float = 448.0) -> torch.Tensor:
+    """BF16 bit patterns where every 1x128 block holds one +-anchor*2^k
+    (k seeded in [-8, 8]) as its largest magnitude, so a block scale derived
+    from the amax is a power of two; the body is N(0, (anchor 2^k / 8)^2)
+    clipped below the anchor, with 1/16 of the elements replaced by exact
+    E4M3 / E5M2 midpoints relative to that power-of-two scale."""
+    blk = idx >> 7
+    pos = idx & 127
+    hb = hash_u32(seed, stream, blk, 21)
+    k = (hb % 17) - 8
+    anchor_pos = (hb >> 8) & 127
+    lg2a = int(math.log2(anchor))                   # 448 = 1.75 * 2^8; 57344 = 1.75 * 2^15
+    a_exp = 127 + lg2a + k                           # FP32 exponent of anchor * 2^k
+    anchor_f32 = (a_exp << 23) | 0x600000            # 1.75 * 2^(lg2a + k)
+    body = gaussian_f32(seed, stream, idx, 1.0)
+    # body scale 1.75 * 2^(lg2a + k - 3) = (anchor 2^k) / 8, built from its bits
+    scale = (((a_exp - 3) << 23) | 0x600000).to(torch.int32).view(torch.float32)
+    b = body * scale
+    lim = anchor_f32.to(torch.int32).view(torch.float32) * torch.tensor(0.99, device=idx.device)
+    b = torch.maximum(torch.minimum(b, lim), -lim)
+    bits = bf16_bits(b)
+    u = hash_u32(seed, stream, idx, 22)
+    # s = anchor*2^k / MAX = 2^k (E4M3, anchor 448): midpoint m * 2^k
+    e_m = (127 + k - 3 + (u >> 4) % 10)
+    mid = ((u >> 31) << 15) | (e_m << 7) | (((u >> 1) & 7) << 4) | 0x8
+    bits = torch.where((u % 16) == 0, mid, bits)
+    a_bits = ((hb >> 31) << 15) | (anchor_f32 >> 16)
+    return torch.where(pos == anchor_pos, a_bits, bits)
+
+
+def saturation_bits(seed: int, stream: int, idx: torch.Tensor) -> torch.Tensor:
+    """BF16 values uniform in [0.9, 1.2] x MAX of E4M3 or E5M2 (chosen per
+    element), random sign, and 1% +-Inf."""
+    u = hash_u32(seed, stream, idx, 31)
+    v = hash_u32(seed, stream, idx, 32)
+    frac = (v & 0xFFFFFF).to(torch.float32) * torch.tensor(2.0 ** -24 * 0.3, device=idx.device)
+    m = torch.where((u & 1) == 1, torch.tensor(448.0, device=idx.device),
+                    torch.tensor(57344.0, device=idx.device))
+    f = (frac + 0.9) * m
+    bits = bf16_bits(f) | ((u >> 31) << 15)
+    inf = ((u >> 30) & 1) << 15 | 0x7F80
+    return torch.where((u >> 8) % 100 == 0, inf, bits)
+
+
+def random_bits(seed: int, stream: int, idx: torch.Tensor) -> torch.Tensor:
+    """Uniformly random 16-bit patterns (NaN, Inf and subnormals included)."""
+    return hash_u32(seed, stream, idx, 41) & 0xFFFF
+
+
+@dataclass
+class BitsSpec:
+    """A 2-D BF16 tensor given by a bit-pattern generator."""
+    name: str
+    rows: int
+    cols: int
+    seed: int
+    stream: int
+    kind: str                      # "mix" | "anchored" | "saturation" | "random"
+
+    def gen(self, idx: torch.Tensor) -> torch.Tensor:
+        if self.kind == "mix":
+            return special_mix_bits(self.seed, self.stream, idx)
+        if self.kind == "anchored":
+            return anchored_bits(self.seed, self.stream, idx)
+        if self.kind == "saturation":
+            return saturation_bits(self.seed, self.stream, idx)
+        return random_bits(self.seed, self.stream, idx)
+
+    def full(self, device) -> torch.Tensor:
+        n = self.rows * self.cols
+        out = torch.empty(n, dtype=torch.bfloat16, device=device)
+        bits16 = out.view(torch.int16)
+        step = 1 << 27
+        for lo in range(0, n, step):
+            idx = torch.arange(lo, min(n, lo + step), dtype=torch.int64, device=device)
+            bits16[lo:lo + idx.numel()].copy_(self.gen(idx))
+        return out.view(self.rows, self.cols)
+
+
+def special_values_4gib() -> list:
+    """Four 16384x32768 BF16 tensors (2^31 elements, 4 GiB): class mix,
+    anchored blocks, saturation edge, random bit patterns."""
+    return [BitsSpec("mix", 16384, 32768, 5005, 500, "mix"),
+            BitsSpec("anchored", 16384, 32768, 5005, 501, "anchored"),
+            BitsSpec("saturation", 16384, 32768, 5005, 502, "saturation"),
+            BitsSpec("random", 16384, 32768, 5005, 503, "random")]
