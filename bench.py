@@ -88,12 +88,117 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
                          wgt_rows.shape[0], wgt_rows.shape[1], t_q)}
 
 
+def _time_launches(fn, reps, flush=None):
+    """Median and minimum milliseconds of fn() over reps runs, HIP events on
+    the current stream; flush() (not timed) runs before each."""
+    import numpy as np
+    import torch
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts)), float(np.min(ts))
+
+
+def measure_configs(dev):
+    """Per-configuration kernel timings outside the step: the tiny case, the
+    8192x8192 per-tensor pair and the 4 GiB special-value tensors.  A 1 GiB
+    write evicts the 256 MB infinity cache before each timed launch."""
+    import torch
+
+    import loss_scaling_fp8_amd as gs
+    import synth
+
+    junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        junk.fill_(1.0)
+
+    res = {}
+    # tiny: 16 FP16 tensors (2^20 elements) unscale + update; 1024^2 per-tensor E4M3
+    g = synth.tiny_gradset()
+    grads = [g.full(t, dev) for t in range(len(g.tensors))]
+    outs = [torch.empty(sp.numel, dtype=torch.float32, device=dev) for sp in g.tensors]
+    S = torch.tensor([g.scale], device=dev)
+    tr = torch.zeros(1, dtype=torch.int32, device=dev)
+    fi = torch.zeros(1, dtype=torch.int32, device=dev)
+    gs.gs_unscale_check(grads, outs, S, fi)
+    torch.cuda.synchronize()
+    ms, _ = _time_launches(lambda: (gs.gs_unscale_check(grads, outs, S, fi),
+                                    gs.gs_update_scale(S, tr, fi, 2.0, 0.5, 2000)), 50)
+    q = synth.tiny_quant()
+    xq = q.full(dev)
+    cq, sq = gs.fp8_quantize(xq, q.fmt, q.gran)
+    ms_q, _ = _time_launches(lambda: gs.fp8_quantize(xq, q.fmt, q.gran, 0, cq, sq), 50)
+    dq = gs.fp8_dequantize(cq, q.fmt, q.gran, sq)
+    ms_d, _ = _time_launches(lambda: gs.fp8_dequantize(cq, q.fmt, q.gran, sq, dq), 50)
+    res["tiny"] = {"unscale+update_us_per_step": round(ms * 1e3, 2),
+                   "quant_per_tensor_1024x1024_us": round(ms_q * 1e3, 2),
+                   "dequant_1024x1024_us": round(ms_d * 1e3, 2),
+                   "note": "launch-bound and cache-resident: correctness case, no GB/s claim"}
+    del grads, outs
+    # per-tensor at scale
+    pt = {}
+    for sp in synth.per_tensor_at_scale():
+        x = sp.full(dev)
+        n = sp.rows * sp.cols
+        codes, scales = gs.fp8_quantize(x, sp.fmt, sp.gran)
+        ws = torch.empty(gs.fp8_quantize_workspace_size(sp.rows, sp.cols, sp.gran),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((sp.rows, sp.cols), dtype=torch.float32, device=dev)
+        mq, mq_min = _time_launches(lambda: gs.fp8_quantize(x, sp.fmt, sp.gran, 0, codes, scales,
+                                                            None, ws), 20, flush)
+        md, _ = _time_launches(lambda: gs.fp8_dequantize(codes, sp.fmt, sp.gran, scales, out),
+                               20, flush)
+        bq, bd = n * 3 + 4, n * 5 + 4
+        pt[sp.name] = {"quant_ms": round(mq, 4), "quant_GBps": round(bq / mq / 1e6, 1),
+                       "quant_hbm_GBps_with_reread": round((bq + 2 * n) / mq / 1e6, 1),
+                       "dequant_ms": round(md, 4), "dequant_GBps": round(bd / md / 1e6, 1)}
+        del x, codes, scales, out
+    res["per_tensor_8192"] = pt
+    # 4 GiB special values, scales from the block amax
+    sv = {}
+    for sp in synth.special_values_4gib():
+        x = sp.full(dev)
+        n = sp.rows * sp.cols
+        codes = torch.empty((sp.rows, sp.cols), dtype=torch.uint8, device=dev)
+        out = torch.empty((sp.rows, sp.cols), dtype=torch.float32, device=dev)
+        ws = torch.empty(gs.fp8_quantize_workspace_size(sp.rows, sp.cols, gs.FP8_PER_TENSOR),
+                         dtype=torch.uint8, device=dev)
+        for fmt in (gs.FP8_E4M3, gs.FP8_E5M2):
+            for gran, gname in ((gs.FP8_PER_TENSOR, "tensor"), (gs.FP8_BLOCK_1x128, "1x128"),
+                                (gs.FP8_BLOCK_128x128, "128x128")):
+                sc = torch.empty(gs.scale_shape(sp.rows, sp.cols, gran), dtype=torch.float32,
+                                 device=dev)
+                gs.fp8_quantize(x, fmt, gran, 0, codes, sc, None, ws)
+                mq, _ = _time_launches(lambda: gs.fp8_quantize(x, fmt, gran, 0, codes, sc, None,
+                                                               ws), 5)
+                md, _ = _time_launches(lambda: gs.fp8_dequantize(codes, fmt, gran, sc, out), 5)
+                ns = sc.numel()
+                key = "%s/%s/%s" % (sp.name, "e4m3" if fmt == 0 else "e5m2", gname)
+                sv[key] = {"quant_GBps": round((n * 3 + ns * 4) / mq / 1e6, 1),
+                           "dequant_GBps": round((n * 5 + ns * 4) / md / 1e6, 1)}
+        del x, codes, out
+        torch.cuda.empty_cache()
+    res["special_4gib"] = sv
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time the tiny, per-tensor 8192^2 and 4 GiB special-value "
+                         "configurations (reported under \"configs\")")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 6 plain copy kernels of 1 GiB (for HBM counter calibration)")
     ap.add_argument("--pmc-safe", action="store_true",
@@ -286,6 +391,11 @@ def main():
         a_host = xa[:2048].cpu().view(torch.int16).numpy().view(np.uint16)
         w_host = xw[:1024].cpu().view(torch.int16).numpy().view(np.uint16)
         result["cpu_baseline"] = cpu_baseline(g_host, a_host, w_host)
+    if args.all_configs:
+        del grads, outs, xa, xw, da, dw
+        torch.cuda.empty_cache()
+        log("other configurations ...")
+        result["configs"] = measure_configs(dev)
     print(json.dumps(result), flush=True)
 
 

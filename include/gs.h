@@ -114,8 +114,10 @@ gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_
 
 /*
  * fp8_quantize_workspace_size -- bytes of device workspace fp8_quantize
- * needs for this shape and granularity in FP8_SCALE_FROM_AMAX mode (per-tensor
- * needs a small buffer of partial maxima; block granularities need none).
+ * needs for this shape and granularity in FP8_SCALE_FROM_AMAX mode: 32 KiB of
+ * per-workgroup partial maxima for per-tensor scaling (the scale depends on
+ * the whole tensor: one pass writes the partial maxima, one workgroup turns
+ * them into the scale, a third pass casts); block granularities need none.
  * Returns 0 when no workspace is needed.
  */
 size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g);

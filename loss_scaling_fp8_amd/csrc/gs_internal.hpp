@@ -38,7 +38,7 @@ hipError_t launch_update_scale(float *scale, int32_t *tracker, int32_t *found_in
                                hipStream_t stream);
 
 // ---------------------------------------------------------------- FP8
-constexpr int kPartialSlots = 1024;   // per-tensor amax partials (workspace words)
+constexpr int kPartialSlots = 8192;   // per-tensor amax partials (workspace words)
 
 hipError_t launch_quantize(const void *x, gs_dtype dt, int64_t rows, int64_t cols, int fmt,
                            int gran, int mode, uint8_t *codes, float *scales,

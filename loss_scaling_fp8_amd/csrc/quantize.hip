@@ -43,8 +43,11 @@
 #ifndef GS_Q128_NT_STORE
 #define GS_Q128_NT_STORE 0
 #endif
+#ifndef GS_QT1_NT_LOAD
+#define GS_QT1_NT_LOAD 1
+#endif
 #ifndef GS_QT_NT_LOAD
-#define GS_QT_NT_LOAD 0
+#define GS_QT_NT_LOAD 1
 #endif
 #ifndef GS_QT_NT_STORE
 #define GS_QT_NT_STORE 0
@@ -155,15 +158,19 @@ struct LaneData {
     }
 
     // FP8 codes of all lane elements, 4 per output word (little-endian).
-    // Fast path (finite lane, scale in the fast range): |x| / s by the
-    // reciprocal and one FMA correction, the sign of x put back, and the
-    // hardware conversion; a clamp only when the scale was given (with a
-    // scale from this block's amax, |x / s| <= MAX (1 + 2^-23)).
+    // Fast path (scale in the fast range): |x| / s by the reciprocal and one
+    // FMA correction, the sign of x put back, and the hardware conversion; a
+    // clamp only when the scale was given (with a scale from this block's
+    // amax, |x / s| <= MAX (1 + 2^-23) for every finite x).  A lane holding
+    // a NaN or an Inf then rewrites just those codes: NaN -> sign|0x7F,
+    // +-Inf -> +-MAX (Inf / s is infinite for a finite positive s, and the
+    // clamp saturates it).  Other scales (0, negative, non-finite, tiny or
+    // huge: only possible when given) take the IEEE division per element.
     template <int FMT, bool CLAMP>
     __device__ __forceinline__ void cast(float s, bool lane_nonfinite,
                                          uint32_t (&out)[kElems / 4]) const {
         const float r = 1.0f / s;
-        if (fast_scale(s) && !lane_nonfinite) {
+        if (fast_scale(s)) {
 #pragma unroll
             for (int j = 0; j < kElems / 4; ++j) {
                 float q[4];
@@ -175,6 +182,18 @@ struct LaneData {
                     q[k] = as_f32(as_u32(a) | (e & 0x80000000u));
                 }
                 out[j] = cvt_pk<FMT, true>(q[2], q[3], cvt_pk<FMT, false>(q[0], q[1], 0u));
+            }
+            if (lane_nonfinite) {
+                constexpr uint32_t kMaxCode = FMT == 0 ? 0x7Eu : 0x7Bu;
+#pragma unroll
+                for (int i = 0; i < kElems; ++i) {
+                    const uint32_t e = elem(i);
+                    if ((e & 0x7F800000u) == 0x7F800000u) {
+                        const uint32_t c = ((e >> 24) & 0x80u) | ((e & 0x7FFFFFu) ? 0x7Fu : kMaxCode);
+                        const int sh = 8 * (i & 3);
+                        out[i >> 2] = (out[i >> 2] & ~(0xFFu << sh)) | (c << sh);
+                    }
+                }
             }
         } else {
 #pragma unroll
@@ -286,30 +305,35 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
 }
 
 // ---------------------------------------------------------------- per-tensor
-// Pass 1: one partial finite max (FP32 bits) per workgroup.
+// Pass 1: one partial finite max (FP32 bits) per workgroup.  A work unit is
+// 4 x 256 consecutive 16-byte vectors (each wave-wide load instruction reads
+// 1 KiB of contiguous input); workgroups take units in a grid-stride loop.
 template <typename IN>
 __global__ __launch_bounds__(256)
 void amax_partials_kernel(const IN *__restrict__ x, int64_t n, uint32_t *__restrict__ partials,
                           int32_t *__restrict__ nonfinite) {
     constexpr int kPerVec = 16 / int(sizeof(IN));
-    constexpr int kUnroll = 4;
+    constexpr int U = 4;
     __shared__ uint32_t red[4];
     const int64_t nvec = n / kPerVec;
     uint32_t m = 0;
     bool nf = false;
-    const int64_t step = int64_t(gridDim.x) * 256;
-    for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec; v += kUnroll * step) {
-        LaneData<IN, 1> L[kUnroll];
+    for (int64_t v0 = int64_t(blockIdx.x) * 256 * U; v0 < nvec; v0 += int64_t(gridDim.x) * 256 * U) {
+        LaneData<IN, 1> L[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (v + u * step < nvec) L[u].template load<GS_QT_NT_LOAD>(x + (v + u * step) * kPerVec);
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * 256 + threadIdx.x;
+            if (v < nvec) L[u].template load<GS_QT1_NT_LOAD>(x + v * kPerVec);
+        }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (v + u * step < nvec) {
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * 256 + threadIdx.x;
+            if (v < nvec) {
                 uint32_t a;
                 nf |= L[u].absmax(a);
                 m = max(m, a);
             }
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
         const IN *p = x + nvec * kPerVec + threadIdx.x;
@@ -326,39 +350,64 @@ void amax_partials_kernel(const IN *__restrict__ x, int64_t n, uint32_t *__restr
     if (nf && nonfinite) *nonfinite = 1;
 }
 
-// Pass 2 (or the only pass in given-scale mode): cast with one scale.
-template <int FMT, int MODE, typename IN>
-__global__ __launch_bounds__(256)
-void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, const uint32_t *__restrict__ partials,
-                         int nparts, uint8_t *__restrict__ codes, float *__restrict__ scales,
-                         int32_t *__restrict__ nonfinite) {
-    constexpr int kPerVec = 16 / int(sizeof(IN));
-    __shared__ uint32_t red[4];
-    float s;
-    if (MODE == FP8_SCALE_FROM_AMAX) {
-        uint32_t m = 0;
-        for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, partials[i]);
-        m = wave_max(m);
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-        __syncthreads();
-        m = max(max(red[0], red[1]), max(red[2], red[3]));
-        s = scale_from_amax<FMT>(as_f32(m));
-        if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
-    } else {
-        s = scales[0];
+// Pass 2 (one 1024-lane workgroup): the tensor amax from the partials (all
+// loads issued before any is used), and its scale.
+template <int FMT>
+__global__ __launch_bounds__(1024)
+void amax_finalize_kernel(const uint32_t *__restrict__ partials, int nparts,
+                          float *__restrict__ scales) {
+    constexpr int kPer = kPartialSlots / 1024;
+    __shared__ uint32_t red[16];
+    uint32_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = k * 1024 + threadIdx.x;
+        v[k] = i < nparts ? partials[i] : 0u;
     }
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) m = max(m, v[k]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int w = 0; w < 16; ++w) r = max(r, red[w]);
+        scales[0] = scale_from_amax<FMT>(as_f32(r));
+    }
+}
+
+// Pass 3 (the only pass with a given scale): cast with the scale in
+// scales[0]; U vectors per lane per work item, each wave-wide load
+// instruction reading 1 KiB of contiguous input.
+template <int FMT, bool CLAMP, typename IN>
+__global__ __launch_bounds__(256)
+void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, uint8_t *__restrict__ codes,
+                         const float *__restrict__ scales, int32_t *__restrict__ nonfinite) {
+    constexpr int kPerVec = 16 / int(sizeof(IN));
+    constexpr int U = 4;
+    const float s = scales[0];
     bool saw_nf = false;
     const int64_t nvec = n / kPerVec;
-    for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < nvec;
-         v += int64_t(gridDim.x) * 256) {
-        LaneData<IN, 1> L;
-        L.template load<GS_QT_NT_LOAD>(x + v * kPerVec);
-        uint32_t a;
-        const bool nf = L.absmax(a);
-        saw_nf |= nf;
-        uint32_t out[kPerVec / 4];
-        L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
-        store_words<GS_QT_NT_STORE>(codes + v * kPerVec, out, kPerVec / 4);
+    for (int64_t v0 = int64_t(blockIdx.x) * 256 * U; v0 < nvec; v0 += int64_t(gridDim.x) * 256 * U) {
+        LaneData<IN, 1> L[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * 256 + threadIdx.x;
+            if (v < nvec) L[u].template load<GS_QT_NT_LOAD>(x + v * kPerVec);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * 256 + threadIdx.x;
+            if (v < nvec) {
+                uint32_t a;
+                const bool nf = L[u].absmax(a);
+                saw_nf |= nf;
+                uint32_t out[kPerVec / 4];
+                L[u].template cast<FMT, CLAMP>(s, nf, out);
+                store_words<GS_QT_NT_STORE>(codes + v * kPerVec, out, kPerVec / 4);
+            }
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
         const int64_t i = nvec * kPerVec + threadIdx.x;
@@ -475,22 +524,24 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
                            dim3(256), 0, stream, x, cols, tpr, ntiles, codes, scales, nonfinite);
         return hipGetLastError();
     }
-    // per-tensor
+    // per-tensor: partial maxima, the scale, the cast (given mode: the cast)
     constexpr int kPerVec = 16 / int(sizeof(IN));
-    int nparts = 0;
     if (MODE == FP8_SCALE_FROM_AMAX) {
-        int64_t p = (n / kPerVec + 256 * 16 - 1) / (256 * 16);     // >= 16 vectors per lane
+        int64_t p = (n / kPerVec + 256 * 4 - 1) / (256 * 4);       // >= 4 vectors per lane
         if (p < 1) p = 1;
         if (p > kPartialSlots) p = kPartialSlots;
-        nparts = (int)p;
-        hipLaunchKernelGGL((amax_partials_kernel<IN>), dim3(nparts), dim3(256), 0, stream, x, n,
-                           partials, nonfinite);
-        const hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL((amax_partials_kernel<IN>), dim3((uint32_t)p), dim3(256), 0, stream, x,
+                           n, partials, nonfinite);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((amax_finalize_kernel<FMT>), dim3(1), dim3(1024), 0, stream, partials,
+                           (int)p, scales);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((quant_tensor_kernel<FMT, MODE, IN>),
-                       dim3(grid_for(n / kPerVec, 256 * 4)), dim3(256), 0, stream, x, n,
-                       partials, nparts, codes, scales, nonfinite);
+    hipLaunchKernelGGL((quant_tensor_kernel<FMT, MODE == FP8_SCALE_GIVEN, IN>),
+                       dim3(grid_for(n / kPerVec, 256 * 4)), dim3(256), 0, stream, x, n, codes,
+                       scales, nonfinite);
     return hipGetLastError();
 }
 

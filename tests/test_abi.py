@@ -41,7 +41,7 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_PER_TENSOR) == 4096
+    assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_PER_TENSOR) == 32768
     assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_BLOCK_1x128) == 0
     assert gs.fp8_quantize_workspace_size(8192, 8192, gs.FP8_BLOCK_128x128) == 0
 
@@ -106,7 +106,7 @@ def test_quantize_workspace_and_output_errors():
     # per-tensor amax mode without workspace
     assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, FAKE, FAKE, None, None, 0, None) == -7
     assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, FAKE, FAKE, None, FAKE, 16, None) == -7
-    assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, None, FAKE, None, FAKE, 4096, None) == -1
+    assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, None, FAKE, None, FAKE, 32768, None) == -1
     assert L.fp8_quantize(FAKE, 2, 64, 64, 0, 0, 0, FAKE, None, None, FAKE, 4096, None) == -1
 
 
