@@ -355,7 +355,7 @@ def main():
         kernels[n] = {"ms": round(per_kernel_ms[n], 4), "bytes": kbytes[n],
                       "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
 
-    src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp", "device_fp8.hpp"])
+    src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp"])
     un = kernels["unscale_check"]
     roofline = {"bound": "hbm", "achieved": un["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(un["GBps"] / PEAK_GBPS, 4), "traffic": pmc_traffic(src_hash),

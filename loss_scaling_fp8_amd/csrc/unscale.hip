@@ -23,7 +23,6 @@
 // registers; a lane that saw a non-finite value stores 1 to the flag (plain
 // vector store, idempotent).  The update is one lane of one wave; nothing
 // ever comes back to the host.
-#include "device_fp8.hpp"
 #include "gs_internal.hpp"
 
 #ifndef GS_UNSCALE_GRID_CAP
