@@ -81,7 +81,7 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
     del np
     return {"value": round(nbytes / (t_un + t_q) / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d FP16 elements of the embedding gradient unscaled (%.1f s), "
+            "sample": "%d FP16 elements (embedding + lm_head gradients) unscaled (%.1f s), "
                       "%dx%d activation rows 1x128 + %dx%d weight rows 128x128 quantized "
                       "and dequantized (%.1f s), E4M3; single-threaded C oracle"
                       % (grad_sample.size, t_un, act_rows.shape[0], act_rows.shape[1],
@@ -387,9 +387,10 @@ def main():
     }
     if not args.no_cpu_baseline and not args.pmc_safe:
         log("cpu baseline (oracle) ...")
-        g_host = grads[0].view(-1).cpu().view(torch.int16).numpy().view(np.uint16)
-        a_host = xa[:2048].cpu().view(torch.int16).numpy().view(np.uint16)
-        w_host = xw[:1024].cpu().view(torch.int16).numpy().view(np.uint16)
+        g_host = np.concatenate([grads[0].view(-1).cpu().view(torch.int16).numpy(),
+                                 grads[-1].view(-1).cpu().view(torch.int16).numpy()]).view(np.uint16)
+        a_host = xa[:8192].cpu().view(torch.int16).numpy().view(np.uint16)
+        w_host = xw[:2048].cpu().view(torch.int16).numpy().view(np.uint16)
         result["cpu_baseline"] = cpu_baseline(g_host, a_host, w_host)
     if args.all_configs:
         del grads, outs, xa, xw, da, dw

@@ -43,6 +43,11 @@
  *   - the 1e-12 floor applies at every granularity;
  *   - a NaN input encodes as sign|0x7F, any other NaN quotient as 0x7F;
  *   - the sign of zero is kept (-0 and negative underflow give 0x80).
+ * Parity unpinned: these reading-defined rules (finite-only amax, NaN
+ * canonicalisation, the floor at per-tensor granularity, the set-only flag
+ * and the skip count) have no value on the pages to check against; they are
+ * pinned only by rule-level unit tests of this file's own behaviour.  Every
+ * function's finite-data behaviour is pinned externally (see the tests).
  */
 #include <math.h>
 #include <stdint.h>
