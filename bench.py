@@ -156,9 +156,17 @@ def measure_configs(dev):
                                                             None, ws), 20, flush)
         md, _ = _time_launches(lambda: gs.fp8_dequantize(codes, sp.fmt, sp.gran, scales, out),
                                20, flush)
+        st = torch.ones(1, dtype=torch.float32, device=dev)
+        hist = torch.zeros(16, dtype=torch.float32, device=dev)
+        pos = torch.zeros(1, dtype=torch.int32, device=dev)
+        used = torch.empty(1, dtype=torch.float32, device=dev)
+        mdl, _ = _time_launches(lambda: gs.fp8_quantize_delayed(x, sp.fmt, st, hist, pos, codes,
+                                                                used, None, ws), 20, flush)
         bq, bd = n * 3 + 4, n * 5 + 4
         pt[sp.name] = {"quant_ms": round(mq, 4), "quant_GBps": round(bq / mq / 1e6, 1),
                        "quant_hbm_GBps_with_reread": round((bq + 2 * n) / mq / 1e6, 1),
+                       "delayed_quant_ms": round(mdl, 4),
+                       "delayed_quant_GBps": round(bq / mdl / 1e6, 1),
                        "dequant_ms": round(md, 4), "dequant_GBps": round(bd / md / 1e6, 1)}
         del x, codes, scales, out
     res["per_tensor_8192"] = pt

@@ -160,6 +160,42 @@ gs_status fp8_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t co
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fp8_quantize_delayed -- per-tensor FP8 quantization with delayed scaling:
+ * the scale applied this step comes from a history of recent amax values,
+ * so the tensor is read once.  "Why FP8 training is stable", Failure 1
+ * (delayed scaling keeps a short history of recent max-abs values and
+ * derives s from it; the scale applied this step reflects earlier steps), and
+ * the "FP8 training" figure of "Mixed precision and FP8 training" (per
+ * tensor, delayed, from recent amax).  One step:
+ *   codes = cast of x with s = *scale_state (the given-scale cast of
+ *           fp8_quantize: divide, clamp to +-MAX, round to nearest even);
+ *   *scale_used = s (dequantize these codes with it);
+ *   amax_t = largest finite |x| (0 if none);
+ *   p = *history_pos mod history_len; amax_history[p] = amax_t;
+ *   *history_pos = (p + 1) mod history_len;
+ *   *scale_state = fl32(max(max(amax_history), fl32(1e-12)) / MAX), the
+ *           scale of the next step (the maximum over the window).
+ *
+ *   x, x_dtype, rows, cols, fmt, codes, nonfinite: as fp8_quantize
+ *              (per-tensor layout; any shape).
+ *   scale_state   device FP32 [1], read and rewritten (start it at the first
+ *                 step's scale, e.g. 1.0).
+ *   amax_history  device FP32 [history_len], zeroed by the caller before the
+ *                 first step; 1 <= history_len <= 1024.
+ *   history_pos   device int32 (0 at the start).
+ *   scale_used    device FP32 [1], written.
+ *   workspace     >= fp8_quantize_workspace_size(rows, cols, FP8_PER_TENSOR)
+ *                 bytes of device scratch (no initialisation needed).
+ * Two launches on `stream` (cast + partial maxima, then the history update);
+ * no host synchronisation.
+ */
+gs_status fp8_quantize_delayed(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                               fp8_format fmt, float *scale_state, float *amax_history,
+                               int32_t history_len, int32_t *history_pos, uint8_t *codes,
+                               float *scale_used, int32_t *nonfinite, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * fp8_dequantize -- out = fl32(decode(code) * s) in FP32, the canonical NaN
  * 0x7FC00000 where that is NaN ("Mixed precision and FP8 training",
  * quant(): cast back to float and multiply by the scale).  E5M2 Inf codes

@@ -24,7 +24,7 @@ FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
 FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 
 EXPORTS = ("gs_unscale_check", "gs_update_scale", "fp8_quantize_workspace_size",
-           "fp8_quantize", "fp8_dequantize", "gs_status_string")
+           "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "gs_status_string")
 
 _lib = None
 
@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
         L.fp8_quantize.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, P, P, P, P, ctypes.c_size_t, P]
         L.fp8_quantize.restype = I32
+        L.fp8_quantize_delayed.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, P, P, I32,
+                                           P, P, P, P, P, ctypes.c_size_t, P]
+        L.fp8_quantize_delayed.restype = I32
         L.fp8_dequantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P]
         L.fp8_dequantize.restype = I32
         L.gs_status_string.argtypes = [I32]
@@ -163,6 +166,33 @@ def fp8_quantize(x, fmt: int, gran: int, mode: int = FP8_SCALE_FROM_AMAX, codes=
                               ws_bytes if workspace is not None else 0, _stream(stream)),
            "fp8_quantize")
     return codes, scales
+
+
+def fp8_quantize_delayed(x, fmt: int, scale_state, amax_history, history_pos, codes=None,
+                         scale_used=None, nonfinite=None, workspace=None, stream=None):
+    """One delayed-scaling step on a 2-D bfloat16/float32 CUDA tensor: cast
+    with the scale in scale_state, record this step's amax in the history
+    ring, write the next step's scale.  Returns (codes, scale_used)."""
+    import torch
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    rows, cols = x.shape
+    dt = GS_BF16 if x.dtype == torch.bfloat16 else GS_F32 if x.dtype == torch.float32 else None
+    if dt is None:
+        raise TypeError("x must be bfloat16 or float32")
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale_used is None:
+        scale_used = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws_bytes = fp8_quantize_workspace_size(rows, cols, FP8_PER_TENSOR)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_quantize_delayed(_ptr(x), dt, rows, cols, int(fmt), _ptr(scale_state),
+                                      _ptr(amax_history), amax_history.numel(),
+                                      _ptr(history_pos), _ptr(codes), _ptr(scale_used),
+                                      _ptr(nonfinite), _ptr(workspace), ws_bytes,
+                                      _stream(stream)), "fp8_quantize_delayed")
+    return codes, scale_used
 
 
 def fp8_dequantize(codes, fmt: int, gran: int, scales, out=None, stream=None):

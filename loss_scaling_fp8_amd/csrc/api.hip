@@ -232,6 +232,32 @@ gs_status fp8_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t co
                                          static_cast<hipStream_t>(stream)));
 }
 
+gs_status fp8_quantize_delayed(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                               fp8_format fmt, float *scale_state, float *amax_history,
+                               int32_t history_len, int32_t *history_pos, uint8_t *codes,
+                               float *scale_used, int32_t *nonfinite, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (x_dtype != GS_BF16 && x_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (bad_enum_fmt(fmt)) return GS_ERR_ARG;
+    if (history_len < 1 || history_len > gsk::kMaxHistory) return GS_ERR_ARG;
+    gs_status st = check_shape(rows, cols, FP8_PER_TENSOR);
+    if (st != GS_OK) return st;
+    const int64_t n = rows * cols;
+    if (n > 0 && (!x || !codes)) return GS_ERR_NULL;
+    if (!scale_state || !amax_history || !history_pos || !scale_used) return GS_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(scale_state, 4) ||
+        misaligned(amax_history, 4) || misaligned(history_pos, 4) || misaligned(scale_used, 4) ||
+        misaligned(nonfinite, 4))
+        return GS_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fp8_quantize_workspace_size(rows, cols, FP8_PER_TENSOR))
+        return GS_ERR_WORKSPACE;
+    if (misaligned(workspace, 4)) return GS_ERR_ALIGN;
+    return from_hip(gsk::launch_quantize_delayed(
+        x, x_dtype, rows, cols, fmt, scale_state, amax_history, history_len, history_pos, codes,
+        scale_used, nonfinite, static_cast<uint32_t *>(workspace),
+        static_cast<hipStream_t>(stream)));
+}
+
 gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
                          fp8_granularity g, const float *scales, float *out, void *stream) {
     if (bad_enum_fmt(fmt) || bad_enum_gran(g)) return GS_ERR_ARG;

@@ -43,6 +43,11 @@ constexpr int kPartialSlots = 8192;   // per-tensor amax partials (workspace wor
 hipError_t launch_quantize(const void *x, gs_dtype dt, int64_t rows, int64_t cols, int fmt,
                            int gran, int mode, uint8_t *codes, float *scales,
                            int32_t *nonfinite, uint32_t *partials, hipStream_t stream);
+constexpr int kMaxHistory = 1024;     // delayed scaling: amax history entries
+hipError_t launch_quantize_delayed(const void *x, gs_dtype dt, int64_t rows, int64_t cols,
+                                   int fmt, float *scale_state, float *history, int32_t hlen,
+                                   int32_t *pos, uint8_t *codes, float *scale_used,
+                                   int32_t *nonfinite, uint32_t *partials, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
                              const float *scales, float *out, hipStream_t stream);
 

@@ -380,14 +380,19 @@ void amax_finalize_kernel(const uint32_t *__restrict__ partials, int nparts,
 // Pass 3 (the only pass with a given scale): cast with the scale in
 // scales[0]; U vectors per lane per work item, each wave-wide load
 // instruction reading 1 KiB of contiguous input.
-template <int FMT, bool CLAMP, typename IN>
+// With EMIT (delayed scaling), each workgroup also writes the largest finite
+// |x| it saw to partials[blockIdx.x]; the grid then has <= kPartialSlots
+// workgroups.
+template <int FMT, bool CLAMP, typename IN, bool EMIT = false>
 __global__ __launch_bounds__(256)
 void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, uint8_t *__restrict__ codes,
-                         const float *__restrict__ scales, int32_t *__restrict__ nonfinite) {
+                         const float *__restrict__ scales, int32_t *__restrict__ nonfinite,
+                         uint32_t *__restrict__ partials = nullptr) {
     constexpr int kPerVec = 16 / int(sizeof(IN));
     constexpr int U = 4;
     const float s = scales[0];
     bool saw_nf = false;
+    uint32_t m = 0;
     const int64_t nvec = n / kPerVec;
     for (int64_t v0 = int64_t(blockIdx.x) * 256 * U; v0 < nvec; v0 += int64_t(gridDim.x) * 256 * U) {
         LaneData<IN, 1> L[U];
@@ -403,6 +408,7 @@ void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, uint8_t *__restric
                 uint32_t a;
                 const bool nf = L[u].absmax(a);
                 saw_nf |= nf;
+                m = max(m, a);
                 uint32_t out[kPerVec / 4];
                 L[u].template cast<FMT, CLAMP>(s, nf, out);
                 store_words<GS_QT_NT_STORE>(codes + v * kPerVec, out, kPerVec / 4);
@@ -415,9 +421,67 @@ void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, uint8_t *__restric
         if constexpr (sizeof(IN) == 2) b = uint32_t(reinterpret_cast<const uint16_t *>(x)[i]) << 16;
         else b = reinterpret_cast<const uint32_t *>(x)[i];
         if ((b & 0x7FFFFFFFu) >= 0x7F800000u) saw_nf = true;
+        else m = max(m, b & 0x7FFFFFFFu);
         codes[i] = (uint8_t)cast_exact<FMT>(as_f32(b), s);
     }
     if (saw_nf && nonfinite) *nonfinite = 1;
+    if constexpr (EMIT) {
+        __shared__ uint32_t red[4];
+        m = wave_max(m);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) partials[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+    }
+}
+
+// Delayed scaling, history update (one 1024-lane workgroup): this step's
+// amax from the partials into the ring, the next step's scale as the
+// maximum over the window, the scale this step used.
+template <int FMT>
+__global__ __launch_bounds__(1024)
+void delayed_update_kernel(const uint32_t *__restrict__ partials, int nparts,
+                           float *__restrict__ scale_state, float *__restrict__ history,
+                           int32_t hlen, int32_t *__restrict__ pos,
+                           float *__restrict__ scale_used) {
+    constexpr int kPer = kPartialSlots / 1024;
+    __shared__ uint32_t red[16];
+    __shared__ uint32_t amax_t;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = k * 1024 + threadIdx.x;
+        v[k] = i < nparts ? partials[i] : 0u;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) m = max(m, v[k]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int w = 0; w < 16; ++w) r = max(r, red[w]);
+        amax_t = r;
+    }
+    __syncthreads();
+    // window maximum with this step's amax in slot p (history values are
+    // non-negative floats, so their bit patterns order like their values)
+    const int32_t p = ((*pos % hlen) + hlen) % hlen;
+    uint32_t h = 0;
+    if (threadIdx.x < hlen)
+        h = (threadIdx.x == p) ? amax_t : as_u32(history[threadIdx.x]);
+    h = wave_max(h);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = h;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t hm = 0;
+        for (int w = 0; w < 16; ++w) hm = max(hm, red[w]);
+        *scale_used = *scale_state;
+        history[p] = as_f32(amax_t);
+        *pos = (p + 1) % hlen;
+        *scale_state = scale_from_amax<FMT>(as_f32(hm));
+    }
 }
 
 // ---------------------------------------------------------------- dequantize
@@ -545,6 +609,25 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
     return hipGetLastError();
 }
 
+template <int FMT, typename IN>
+hipError_t quantize_delayed_typed(const IN *x, int64_t rows, int64_t cols, float *scale_state,
+                                  float *history, int32_t hlen, int32_t *pos, uint8_t *codes,
+                                  float *scale_used, int32_t *nonfinite, uint32_t *partials,
+                                  hipStream_t stream) {
+    constexpr int kPerVec = 16 / int(sizeof(IN));
+    const int64_t n = rows * cols;
+    int64_t g = (n / kPerVec + 256 * 4 - 1) / (256 * 4);
+    if (g < 1) g = 1;
+    if (g > kPartialSlots) g = kPartialSlots;
+    hipLaunchKernelGGL((quant_tensor_kernel<FMT, true, IN, true>), dim3((uint32_t)g), dim3(256),
+                       0, stream, x, n, codes, scale_state, nonfinite, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((delayed_update_kernel<FMT>), dim3(1), dim3(1024), 0, stream, partials,
+                       (int)g, scale_state, history, hlen, pos, scale_used);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int gran,
                           const float *scales, float *out, hipStream_t stream) {
@@ -583,6 +666,22 @@ hipError_t launch_quantize(const void *x, gs_dtype dt, int64_t rows, int64_t col
     }
 #undef GS_Q_T
 #undef GS_Q
+}
+
+hipError_t launch_quantize_delayed(const void *x, gs_dtype dt, int64_t rows, int64_t cols,
+                                   int fmt, float *scale_state, float *history, int32_t hlen,
+                                   int32_t *pos, uint8_t *codes, float *scale_used,
+                                   int32_t *nonfinite, uint32_t *partials, hipStream_t stream) {
+#define GS_QD(F, T)                                                                            \
+    return quantize_delayed_typed<F, T>(static_cast<const T *>(x), rows, cols, scale_state,   \
+                                        history, hlen, pos, codes, scale_used, nonfinite,     \
+                                        partials, stream)
+    if (fmt == FP8_E4M3) {
+        if (dt == GS_BF16) GS_QD(0, uint16_t); else GS_QD(0, float);
+    } else {
+        if (dt == GS_BF16) GS_QD(1, uint16_t); else GS_QD(1, float);
+    }
+#undef GS_QD
 }
 
 hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,

@@ -56,6 +56,9 @@ PINS = {
     "quantize": "page fp8_scaling.py listing run by torch CPU; page error table; "
                 "outlier exercise; scale-invariance and error-bound properties",
     "dequantize": "page quant() listing run by torch CPU",
+    "quantize_delayed": "reduces to the pinned per-tensor quantizer (history 1, same "
+                        "tensor twice); window max closed form; the pages' spike failure "
+                        "shape (saturation); otherwise parity unpinned",
 }
 
 _lib = None
@@ -103,6 +106,9 @@ def lib() -> ctypes.CDLL:
             L.orc_quantize.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, P, P, P]
             L.orc_quantize.restype = ctypes.c_int
+            L.orc_quantize_delayed.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, P, P,
+                                               I32, P, P, P, P]
+            L.orc_quantize_delayed.restype = ctypes.c_int
             L.orc_dequantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P]
             L.orc_dequantize.restype = ctypes.c_int
             L.orc_fp8_encode_array.argtypes = [P, I64, ctypes.c_int, P]
@@ -256,6 +262,32 @@ def quantize(x: np.ndarray, fmt: int, gran: int, mode: int = FROM_AMAX,
 def block_amax(x: np.ndarray, r0: int, nr: int, c0: int, nc: int) -> np.float32:
     x, dt = _as_input(x)
     return np.float32(lib().orc_block_amax(_ptr(x), dt, x.shape[1], r0, nr, c0, nc))
+
+
+class DelayedState:
+    """Delayed per-tensor scaling state: the scale for the next step, the
+    amax history ring and its position."""
+
+    def __init__(self, history_len: int, init_scale: float = 1.0):
+        self.scale = np.float32([init_scale])
+        self.history = np.zeros(history_len, np.float32)
+        self.pos = np.int32([0])
+
+
+def quantize_delayed(x: np.ndarray, fmt: int, st: DelayedState):
+    """One delayed-scaling step; returns (codes, scale used, nonfinite) and
+    updates st (history, position, next scale)."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.uint8)
+    used = np.zeros(1, np.float32)
+    nf = ctypes.c_int32(0)
+    rc = lib().orc_quantize_delayed(_ptr(x), dt, rows, cols, fmt, _ptr(st.scale),
+                                    _ptr(st.history), st.history.size, _ptr(st.pos),
+                                    _ptr(codes), _ptr(used), ctypes.byref(nf))
+    if rc != 0:
+        raise ValueError("bad delayed-scaling state")
+    return codes, used[0], nf.value
 
 
 def dequantize(codes: np.ndarray, fmt: int, gran: int, scales: np.ndarray) -> np.ndarray:

@@ -324,6 +324,41 @@ int orc_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
     return 0;
 }
 
+/* Delayed per-tensor scaling, [WHY] Failure 1 ("keep a short history of
+ * recent max-abs values and derive s from that"; the scale applied this step
+ * comes from earlier steps) and the [MP] "FP8 training" figure ("per tensor
+ * (delayed, from recent amax)").  One step:
+ *   1. codes = quant(x, s) with s = *scale_state (the given-scale cast:
+ *      divide, clamp, round to nearest even);
+ *   2. amax_t = largest finite |x| (0 if none);
+ *   3. history[p] = amax_t with p = *pos mod H; *pos = (p + 1) mod H;
+ *   4. *scale_state = fl32(max(max over the H history entries, 1e-12) / MAX),
+ *      the scale for the next step.
+ * Reading: "derive s from that" is taken as the maximum over the window (the
+ * scale then covers every recent amax).  *scale_used receives the s of
+ * step 1 (the dequantisation multiplier of these codes). */
+int orc_quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
+                         float *scale_state, float *history, int32_t hlen, int32_t *pos,
+                         uint8_t *codes, float *scale_used, int32_t *nonfinite)
+{
+    if (hlen <= 0)
+        return -1;
+    const int32_t p = ((*pos % hlen) + hlen) % hlen;   /* position taken modulo H */
+    const float s = *scale_state;
+    if (orc_quantize(x, dtype, rows, cols, fmt, ORC_PER_TENSOR, ORC_GIVEN, codes,
+                     scale_state, nonfinite) != 0)
+        return -1;
+    *scale_used = s;
+    history[p] = orc_block_amax(x, dtype, cols, 0, rows, 0, cols);
+    *pos = (p + 1) % hlen;
+    float hmax = 0.0f;
+    for (int32_t i = 0; i < hlen; ++i)
+        if (history[i] > hmax)
+            hmax = history[i];
+    *scale_state = orc_scale_from_amax(hmax, fmt);
+    return 0;
+}
+
 /* Dequantize, [MP] quant(): the FP8 value times its block's scale, in FP32.
  * out = fl32(decode(code) * s), canonical NaN for NaN results. */
 int orc_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,

@@ -117,3 +117,29 @@ def test_dequantize_argument_errors():
     assert L.fp8_dequantize(None, 128, 128, 0, 1, FAKE, FAKE, None) == -1
     assert L.fp8_dequantize(FAKE, 128, 128, 0, 1, FAKE, FAKE + 8, None) == -6
     assert L.fp8_dequantize(None, 0, 128, 0, 1, None, None, None) == 0   # empty: nothing to do
+
+
+def test_quantize_delayed_argument_errors():
+    L = gs.lib()
+    f = L.fp8_quantize_delayed
+    args = dict(x=FAKE, dt=2, r=64, c=64, fmt=0, st=FAKE, hist=FAKE, hl=16, pos=FAKE,
+                codes=FAKE, used=FAKE, nf=None, ws=FAKE, wsb=32768)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["dt"], a["r"], a["c"], a["fmt"], a["st"], a["hist"], a["hl"],
+                 a["pos"], a["codes"], a["used"], a["nf"], a["ws"], a["wsb"], None)
+    assert call(dt=1) == -4
+    assert call(fmt=3) == -5
+    assert call(hl=0) == -5
+    assert call(hl=1025) == -5
+    assert call(r=-1) == -2
+    assert call(x=None) == -1
+    assert call(st=None) == -1
+    assert call(hist=None) == -1
+    assert call(pos=None) == -1
+    assert call(used=None) == -1
+    assert call(x=FAKE + 8) == -6
+    assert call(pos=FAKE + 2) == -6
+    assert call(ws=None) == -7
+    assert call(wsb=100) == -7

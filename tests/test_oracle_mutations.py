@@ -35,11 +35,14 @@ MUTANTS = {
     "scale_inverted": ("return a / (float)fmt_max(fmt);", "return (float)fmt_max(fmt) / a;"),
     "multiply_by_reciprocal": ("float y = f / s;", "float y = f * (1.0f / s);"),
     "dequant_block_transposed": ("(r / br) * nbc + c / bc;", "(c / bc) * nbc + r / br;"),
+    "delayed_latest_only": ("        if (history[i] > hmax)", "        if (i == p && history[i] > hmax)"),
+    "delayed_ring_stuck": ("    *pos = (p + 1) % hlen;", "    *pos = p;"),
+    "delayed_uses_new_scale": ("    *scale_used = s;", "    *scale_used = *scale_state * 2.0f;"),
     "nan_input_unsigned": ("return (uint8_t)((signbit(f) ? 0x80 : 0x00) | 0x7F);", "return 0x7F;"),
 }
 
 FAST_PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_unscale.py",
-             "tests/test_oracle_quant.py"]
+             "tests/test_oracle_quant.py", "tests/test_oracle_delayed.py"]
 
 
 def _run_mutant(name, tmp_dir):
