@@ -52,6 +52,8 @@ PINS = {
     "f16_to_f32": "numpy float16 widening, all 65536 patterns",
     "unscale_check": "page worked examples (1e-8 via 1024; 1e-8/1e-6/2e-5 via 2^16); "
                      "numpy f32 multiply over all FP16 patterns x scales",
+    "unscale_check_sumsq": "exact integer sum of squares against Python integers; "
+                           "norm_sq against numpy float64 sums within 1e-12",
     "update_scale": "page 5-step trace; closed-form trajectories (collapse, overflow, C1)",
     "quantize": "page fp8_scaling.py listing run by torch CPU; page error table; "
                 "outlier exercise; scale-invariance and error-bound properties",
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
             L.orc_fp8_encode.restype = ctypes.c_uint8
             L.orc_unscale_check.argtypes = [I32, P, P, P, F, P]
             L.orc_unscale_check.restype = None
+            L.orc_unscale_check_sumsq.argtypes = [I32, P, P, P, F, P, P, P]
+            L.orc_unscale_check_sumsq.restype = None
             L.orc_update_scale.argtypes = [P, P, P, F, F, I32, P]
             L.orc_update_scale.restype = None
             L.orc_block_amax.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, I64]
@@ -200,6 +204,24 @@ def unscale_check(grads: list[np.ndarray], S: float, found_inf: int = 0):
     flag = ctypes.c_int32(found_inf)
     lib().orc_unscale_check(n, gp, op, ne, float(np.float32(S)), ctypes.byref(flag))
     return outs, flag.value
+
+
+def unscale_check_sumsq(grads: list[np.ndarray], S: float, found_inf: int = 0,
+                        sumsq: tuple = (0, 0)):
+    """unscale_check plus the exact sum of squares: returns (outputs,
+    found_inf, (sumsq_lo, sumsq_hi) running total, norm_sq)."""
+    gs = [np.ascontiguousarray(g).view(np.uint16).reshape(-1) for g in grads]
+    outs = [np.empty(g.size, np.float32) for g in gs]
+    n = len(gs)
+    gp = (ctypes.c_void_p * max(n, 1))(*[g.ctypes.data for g in gs])
+    op = (ctypes.c_void_p * max(n, 1))(*[o.ctypes.data for o in outs])
+    ne = (ctypes.c_int64 * max(n, 1))(*[g.size for g in gs])
+    flag = ctypes.c_int32(found_inf)
+    acc = (ctypes.c_uint64 * 2)(*sumsq)
+    nsq = ctypes.c_double(0.0)
+    lib().orc_unscale_check_sumsq(n, gp, op, ne, float(np.float32(S)), ctypes.byref(flag),
+                                  acc, ctypes.byref(nsq))
+    return outs, flag.value, (acc[0], acc[1]), nsq.value
 
 
 class ScalerState:

@@ -203,6 +203,44 @@ void orc_unscale_check(int32_t n, const uint16_t *const *grads,
         *found_inf = 1;
 }
 
+/* Unscale + check as orc_unscale_check, plus the sum of squares of the
+ * gradients for norm clipping ("Loss Scaling", "Where it fits": loss scaling
+ * pairs with gradient clipping; "Numerical Precision, Mixed Precision, and
+ * Loss Scaling", the AMP sequence: unscale and inspect, then clip and update).
+ * Exact definition: every finite FP16 value g is an integer multiple of
+ * 2^-24 below 2^16 in magnitude, so G = |g| * 2^24 is an integer below 2^40
+ * and X = sum G^2 over the finite inputs is an integer below 2^113 (for up
+ * to 2^33 elements): it is accumulated exactly in 128 bits and ADDED to
+ * sumsq[0] (low 64 bits) + sumsq[1] * 2^64.  The recovered-gradient norm
+ * squared is then
+ *   *norm_sq = fl64(fl64(X_total) * 2^-48) * fl64(inv * inv),
+ * with fl64(X_total) the round-to-nearest-even conversion of the 128-bit
+ * running total and inv = fl32(1/S) (inv * inv is exact in FP64); for a
+ * power-of-two S this is the correctly rounded sum of y^2. */
+void orc_unscale_check_sumsq(int32_t n, const uint16_t *const *grads,
+                             float *const *outs, const int64_t *numels,
+                             float S, int32_t *found_inf, uint64_t *sumsq,
+                             double *norm_sq)
+{
+    orc_unscale_check(n, grads, outs, numels, S, found_inf);
+    unsigned __int128 X = 0;
+    for (int32_t t = 0; t < n; ++t)
+        for (int64_t i = 0; i < numels[t]; ++i) {
+            double g = (double)orc_f16_to_f32(grads[t][i]);
+            if (!isfinite(g))
+                continue;
+            uint64_t G = (uint64_t)(fabs(g) * 16777216.0);   /* exact */
+            X += (unsigned __int128)G * G;
+        }
+    unsigned __int128 total = ((unsigned __int128)sumsq[1] << 64) | sumsq[0];
+    total += X;
+    sumsq[0] = (uint64_t)total;
+    sumsq[1] = (uint64_t)(total >> 64);
+    float inv = 1.0f / S;
+    double d = (double)total;                 /* round to nearest even */
+    *norm_sq = (d * 0x1p-48) * ((double)inv * (double)inv);
+}
+
 /* Grow/backoff update of the loss scale, [LS] SimpleGradScaler.step with
  * [NP]'s GradScaler factors (backoff 0.5 instead of the listing's /2.0; the
  * two give the same FP32 result since both round the same exact value):

@@ -38,11 +38,15 @@ MUTANTS = {
     "delayed_latest_only": ("        if (history[i] > hmax)", "        if (i == p && history[i] > hmax)"),
     "delayed_ring_stuck": ("    *pos = (p + 1) % hlen;", "    *pos = p;"),
     "delayed_uses_new_scale": ("    *scale_used = s;", "    *scale_used = *scale_state * 2.0f;"),
+    "sumsq_wrong_unit": ("uint64_t G = (uint64_t)(fabs(g) * 16777216.0);", "uint64_t G = (uint64_t)(fabs(g) * 8388608.0);"),
+    "sumsq_not_accumulated": ("    total += X;", "    total = X;"),
+    "norm_without_inverse": ("*norm_sq = (d * 0x1p-48) * ((double)inv * (double)inv);", "*norm_sq = (d * 0x1p-48);"),
     "nan_input_unsigned": ("return (uint8_t)((signbit(f) ? 0x80 : 0x00) | 0x7F);", "return 0x7F;"),
 }
 
 FAST_PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_unscale.py",
-             "tests/test_oracle_quant.py", "tests/test_oracle_delayed.py"]
+             "tests/test_oracle_quant.py", "tests/test_oracle_delayed.py",
+             "tests/test_oracle_sumsq.py"]
 
 
 def _run_mutant(name, tmp_dir):
