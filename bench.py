@@ -209,6 +209,8 @@ def main():
                          "configurations (reported under \"configs\")")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 6 plain copy kernels of 1 GiB (for HBM counter calibration)")
+    ap.add_argument("--sumsq", action="store_true",
+                    help="with --pmc-safe: also run the unscale + sum-of-squares variant")
     ap.add_argument("--pmc-safe", action="store_true",
                     help="for rocprofv3 --pmc runs: constant inputs (few kernel launches), no "
                          "device-to-device or device-to-host memcpy, no copy ceiling, no "
@@ -363,6 +365,29 @@ def main():
         kernels[n] = {"ms": round(per_kernel_ms[n], 4), "bytes": kbytes[n],
                       "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
 
+    # unscale fused with the exact gradient sum of squares, on the same
+    # resident gradient set (outside the timed step; own HIP events)
+    ext = {}
+    if not args.pmc_safe or args.sumsq:
+        acc = torch.zeros(2, dtype=torch.int64, device=dev)
+        nsq = torch.empty(1, dtype=torch.float64, device=dev)
+        ws = torch.empty(gs.gs_unscale_check_sumsq_workspace_size([g.numel() for g in grads]),
+                         dtype=torch.uint8, device=dev)
+        S.fill_(gset.scale)
+        found.zero_()
+        gs.gs_unscale_check_sumsq(grads, outs, S, found, acc, nsq, ws)
+        ms_sq, ms_sq_min = _time_launches(
+            lambda: gs.gs_unscale_check_sumsq(grads, outs, S, found, acc, nsq, ws), 10)
+        gbps = bytes_unscale / (ms_sq * 1e-3) / 1e9
+        ext["unscale_check_sumsq"] = {
+            "ms": round(ms_sq, 4), "bytes": bytes_unscale, "GBps": round(gbps, 1),
+            "frac_of_peak": round(gbps / PEAK_GBPS, 4),
+            "vs_unscale_check": round(per_kernel_ms["unscale_check"] / ms_sq, 4),
+            "note": "three launches (unscale + per-chunk partials, 128-bit reduction, final); "
+                    "bytes count the FP16 read and FP32 write only"}
+        log("unscale+sumsq: %.3f ms (%.0f GB/s)" % (ms_sq, gbps))
+        del ws
+
     src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp"])
     un = kernels["unscale_check"]
     roofline = {"bound": "hbm", "achieved": un["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
@@ -390,6 +415,7 @@ def main():
                    "act_shape": [act.rows, act.cols], "wgt_shape": [wgt.rows, wgt.cols]},
         "roofline": roofline,
         "kernels": kernels,
+        "extensions": ext,
         "copy_ceiling_GBps": copy_gbps,
         "final_state": {"S": state[0], "tracker": state[1], "skips": state[2]},
     }

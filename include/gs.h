@@ -92,6 +92,49 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
                            int32_t *found_inf, void *stream);
 
 /*
+ * gs_unscale_check_sumsq_workspace_size -- bytes of device workspace
+ * gs_unscale_check_sumsq needs for a list with these element counts:
+ * 16 * (sum over tensors of ceil(numels[i] / 2048) + 1024).  Returns 0 for
+ * invalid counts (n < 0, a negative count, numels NULL with n > 0).
+ */
+size_t gs_unscale_check_sumsq_workspace_size(int32_t n, const int64_t *numels);
+
+/*
+ * gs_unscale_check_sumsq -- gs_unscale_check plus the exact sum of squares
+ * of the gradients, for norm clipping.  The AMP step sequence of "Numerical
+ * Precision, Mixed Precision, and Loss Scaling" unscales and inspects the
+ * gradients, then clips them before the update, and "Loss Scaling" (section
+ * "Where it fits") pairs loss scaling with gradient clipping; clipping by
+ * global norm needs the norm of the recovered gradients, computed here in the
+ * same pass over the FP16 data.
+ * Outputs and found_inf exactly as gs_unscale_check.  In addition:
+ *   X = sum over the FINITE inputs g of (|g| * 2^24)^2, an exact integer
+ *       (every finite FP16 value is a multiple of 2^-24 below 2^16);
+ *   sumsq[0] + sumsq[1] * 2^64 += X (128-bit running total, device uint64
+ *       [2], 8-byte aligned; the caller zeroes it once per step, so several
+ *       calls, e.g. one per gradient bucket, accumulate);
+ *   *norm_sq = fl64(fl64(total) * 2^-48) * (inv * inv), with fl64(total)
+ *       the round-to-nearest-even FP64 value of the new running total and
+ *       inv = fl32(1/S) widened to FP64 (device double, 8-byte aligned).
+ *       For a power-of-two S this is the correctly rounded sum of y^2 over
+ *       the finite outputs; it does not depend on the launch configuration.
+ *   Inf and NaN inputs are left out of X (they set found_inf; such a step
+ *   is skipped anyway).
+ *   workspace: device buffer of at least
+ *       gs_unscale_check_sumsq_workspace_size(n, numels) bytes, 16-byte
+ *       aligned, scratch (no initialisation needed).
+ * Other arguments, the descriptor cache and errors as gs_unscale_check.
+ * An empty list still updates *norm_sq from the running total.  Three
+ * launches on `stream` (the unscale pass writing one partial per chunk, a
+ * second-level reduction, a one-workgroup final add); no host
+ * synchronisation.
+ */
+gs_status gs_unscale_check_sumsq(int32_t n, const void *const *grads, float *const *outs,
+                                 const int64_t *numels, gs_dtype in_dtype, const float *scale,
+                                 int32_t *found_inf, uint64_t *sumsq, double *norm_sq,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gs_update_scale -- grow/backoff/skip state machine, kept on the device.
  * SimpleGradScaler.step ("Loss scaling, FP8, and the failure that never
  * crashes", worked example) with the GradScaler defaults paragraph of

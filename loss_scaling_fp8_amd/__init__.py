@@ -23,7 +23,8 @@ FP8_E4M3, FP8_E5M2 = 0, 1
 FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
 FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 
-EXPORTS = ("gs_unscale_check", "gs_update_scale", "fp8_quantize_workspace_size",
+EXPORTS = ("gs_unscale_check", "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
+           "gs_update_scale", "fp8_quantize_workspace_size",
            "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "gs_status_string")
 
 _lib = None
@@ -46,6 +47,11 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.gs_unscale_check.argtypes = [I32, P, P, P, ctypes.c_int, P, P, P]
         L.gs_unscale_check.restype = I32
+        L.gs_unscale_check_sumsq_workspace_size.argtypes = [I32, P]
+        L.gs_unscale_check_sumsq_workspace_size.restype = ctypes.c_size_t
+        L.gs_unscale_check_sumsq.argtypes = [I32, P, P, P, ctypes.c_int, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        L.gs_unscale_check_sumsq.restype = I32
         L.gs_update_scale.argtypes = [P, P, P, F, F, I32, P, P]
         L.gs_update_scale.restype = I32
         L.fp8_quantize_workspace_size.argtypes = [I64, I64, ctypes.c_int]
@@ -104,6 +110,12 @@ def scale_shape(rows: int, cols: int, gran: int) -> tuple:
 def gs_unscale_check(grads: Sequence, outs: Sequence, scale, found_inf, stream=None) -> None:
     """FP16 gradients -> FP32 outputs multiplied by fl32(1/S); found_inf set to
     1 on any non-finite output.  One kernel launch for the whole list."""
+    n, arr_g, arr_o, arr_n = _grad_lists(grads, outs)
+    _check(lib().gs_unscale_check(n, arr_g, arr_o, arr_n, GS_F16, _ptr(scale), _ptr(found_inf),
+                                  _stream(stream)), "gs_unscale_check")
+
+
+def _grad_lists(grads, outs):
     import torch
     n = len(grads)
     if len(outs) != n:
@@ -116,8 +128,33 @@ def gs_unscale_check(grads: Sequence, outs: Sequence, scale, found_inf, stream=N
     arr_g = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
     arr_o = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
     arr_n = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
-    _check(lib().gs_unscale_check(n, arr_g, arr_o, arr_n, GS_F16, _ptr(scale), _ptr(found_inf),
-                                  _stream(stream)), "gs_unscale_check")
+    return n, arr_g, arr_o, arr_n
+
+
+def gs_unscale_check_sumsq_workspace_size(numels: Sequence[int]) -> int:
+    n = len(numels)
+    arr_n = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    return int(lib().gs_unscale_check_sumsq_workspace_size(n, arr_n))
+
+
+def gs_unscale_check_sumsq(grads: Sequence, outs: Sequence, scale, found_inf, sumsq, norm_sq,
+                           workspace=None, stream=None) -> None:
+    """gs_unscale_check plus the exact 128-bit sum of squares of the finite
+    gradients, added to sumsq (int64 [2], low and high words), and the
+    recovered-gradient norm squared written to norm_sq (float64 [1])."""
+    import torch
+    n, arr_g, arr_o, arr_n = _grad_lists(grads, outs)
+    if sumsq.dtype not in (torch.int64, torch.uint64) or sumsq.numel() != 2:
+        raise TypeError("sumsq must be a 2-element int64 tensor")
+    if norm_sq.dtype != torch.float64:
+        raise TypeError("norm_sq must be float64")
+    ws_bytes = gs_unscale_check_sumsq_workspace_size([g.numel() for g in grads])
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scale.device)
+    _check(lib().gs_unscale_check_sumsq(n, arr_g, arr_o, arr_n, GS_F16, _ptr(scale),
+                                        _ptr(found_inf), _ptr(sumsq), _ptr(norm_sq),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)),
+           "gs_unscale_check_sumsq")
 
 
 def gs_update_scale(scale, growth_tracker, found_inf, growth_factor: float = 2.0,

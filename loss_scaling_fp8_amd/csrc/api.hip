@@ -185,6 +185,48 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
                                               static_cast<hipStream_t>(stream)));
 }
 
+size_t gs_unscale_check_sumsq_workspace_size(int32_t n, const int64_t *numels) {
+    if (n < 0 || (n > 0 && !numels)) return 0;
+    int64_t chunks = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (numels[i] < 0 || numels[i] > kMaxElems) return 0;
+        chunks += (numels[i] + gsk::kUnscaleChunk - 1) / gsk::kUnscaleChunk;
+    }
+    return size_t(chunks + gsk::kSumsqL2) * gsk::kSumsqPartBytes;
+}
+
+gs_status gs_unscale_check_sumsq(int32_t n, const void *const *grads, float *const *outs,
+                                 const int64_t *numels, gs_dtype in_dtype, const float *scale,
+                                 int32_t *found_inf, uint64_t *sumsq, double *norm_sq,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (n < 0) return GS_ERR_SIZE;
+    if (in_dtype != GS_F16) return GS_ERR_DTYPE;
+    if (!scale || !found_inf || !sumsq || !norm_sq) return GS_ERR_NULL;
+    if (misaligned(scale, 4) || misaligned(found_inf, 4) || misaligned(sumsq, 8) ||
+        misaligned(norm_sq, 8))
+        return GS_ERR_ALIGN;
+    if (n > 0 && (!grads || !outs || !numels)) return GS_ERR_NULL;
+    int64_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (numels[i] < 0 || numels[i] > kMaxElems) return GS_ERR_SIZE;
+        if (numels[i] > 0 && (!grads[i] || !outs[i])) return GS_ERR_NULL;
+        if (misaligned(grads[i], 2) || misaligned(outs[i], 4)) return GS_ERR_ALIGN;
+        total += numels[i];
+        if (total > kMaxElems * 64) return GS_ERR_SIZE;
+    }
+    if (!workspace || workspace_bytes < gs_unscale_check_sumsq_workspace_size(n, numels))
+        return GS_ERR_WORKSPACE;
+    if (misaligned(workspace, 16)) return GS_ERR_ALIGN;
+    CachedList cl;
+    if (total > 0) {
+        const gs_status st = get_list(n, grads, outs, numels, cl);
+        if (st != GS_OK) return st;
+    }
+    return from_hip(gsk::launch_unscale_check_sumsq(
+        static_cast<const gsk::ChunkDesc *>(cl.dev), cl.nchunks, scale, found_inf, sumsq, norm_sq,
+        workspace, static_cast<hipStream_t>(stream)));
+}
+
 gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_inf,
                           float growth_factor, float backoff_factor, int32_t growth_interval,
                           int64_t *skip_count, void *stream) {

@@ -33,6 +33,14 @@ constexpr uint64_t kAddrMask = (uint64_t(1) << 48) - 1;
 
 hipError_t launch_unscale_check(const ChunkDesc *descs, int64_t nchunks, const float *scale,
                                 int32_t *found_inf, hipStream_t stream);
+// Unscale + exact gradient sum of squares: one 16-byte partial per chunk
+// (workspace), then kSumsqL2 second-level 128-bit partials, then one
+// workgroup adds them to the running total and writes the norm squared.
+constexpr int kSumsqL2 = 1024;
+constexpr size_t kSumsqPartBytes = 16;
+hipError_t launch_unscale_check_sumsq(const ChunkDesc *descs, int64_t nchunks, const float *scale,
+                                      int32_t *found_inf, uint64_t *sumsq, double *norm_sq,
+                                      void *workspace, hipStream_t stream);
 hipError_t launch_update_scale(float *scale, int32_t *tracker, int32_t *found_inf, float growth,
                                float backoff, int32_t interval, int64_t *skips,
                                hipStream_t stream);

@@ -38,8 +38,8 @@ __device__ __forceinline__ float widen_f16(uint32_t h16) {
 }
 
 // y = fl32(g * inv); canonical NaN on output; accumulate "not finite".
-__device__ __forceinline__ float unscale_one(uint32_t h16, float inv, bool &bad) {
-    const float y = widen_f16(h16) * inv;
+__device__ __forceinline__ float unscale_f(float g, float inv, bool &bad) {
+    const float y = g * inv;
     bad |= !__builtin_isfinite(y);
     return __builtin_isnan(y) ? __uint_as_float(0x7FC00000u) : y;
 }
@@ -53,37 +53,232 @@ typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 typedef __attribute__((address_space(1))) const uint16_t g_cu16;
 typedef __attribute__((address_space(1))) float g_f32;
 
+// ---- exact sum of squares (the SUMSQ variant)
+// A finite FP16 g is a multiple of 2^-24 below 2^16, so q = g*g is exact in
+// FP32 (22-bit significand, in [2^-48, 2^32]) and G^2 = q * 2^48 is an
+// integer.  Each q is split exactly in FP64 at the 2^-18 grid: t = q + C
+// with C = 1.5 * 2^34 (ulp 2^-18; t stays in [2^34, 2^35)), hi = t - C,
+// lo = q - hi (|lo| <= 2^-19, a multiple of 2^-48).  Per lane, over the 8
+// elements of a chunk, sum(lo) is exact in FP64 and sum(hi) is carried as
+// the integer sum of bits(t) - bits(C) (= hi * 2^18 per element), so the
+// chunk's sum of G^2 = B * 2^30 + A with B = sum(hi) * 2^18 < 2^61 and
+// |A| = |sum(lo)| * 2^48 <= 2^40, both exact 64-bit integers.
+constexpr double kSplitC = 0x1.8p34;
+constexpr uint64_t kSplitBits = 0x4218000000000000ull;   // bits of 1.5 * 2^34
+constexpr double kIntMagic = 0x1.8p52;                  // integer extraction, |v| < 2^51
+constexpr uint64_t kIntMagicBits = 0x4338000000000000ull;
+
+__device__ __forceinline__ void sq_add(float f, double &lo, uint64_t &hib) {
+    const double d = (double)(f * f);
+    const double t = d + kSplitC;
+    const double hi = t - kSplitC;
+    lo += d - hi;
+    hib += (uint64_t)__double_as_longlong(t);
+}
+
+// Sum over each row of 16 lanes (every lane of the row gets the row's sum),
+// by DPP lane exchanges on the two 32-bit halves; all 64 lanes active.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t row_sum_u64(uint64_t v) {
+    v += dpp_u64<0xB1>(v);     // quad_perm 1,0,3,2
+    v += dpp_u64<0x4E>(v);     // quad_perm 2,3,0,1
+    v += dpp_u64<0x141>(v);    // row_half_mirror: the other quad of each 8
+    v += dpp_u64<0x140>(v);    // row_mirror: the other 8 of the row
+    return v;
+}
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+template <bool SUMSQ>
 __global__ __launch_bounds__(kUnscaleThreads)
 void unscale_check_kernel(const ChunkDesc *__restrict__ descs, int64_t nchunks,
-                          const float *__restrict__ scale, int32_t *__restrict__ found_inf) {
+                          const float *__restrict__ scale, int32_t *__restrict__ found_inf,
+                          u64x2 *__restrict__ parts) {
     const float inv = 1.0f / *scale;         // IEEE division, once per lane
     bool bad = false;
     const int tid = threadIdx.x;
+    __shared__ uint64_t red[2][kUnscaleThreads / 16];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const ChunkDesc d = descs[c];
         g_cu16 *in = (g_cu16 *)(uintptr_t)(d.in_bits & kAddrMask);
         g_f32 *out = (g_f32 *)(uintptr_t)(d.out_bits & ~uint64_t(3));
         const int64_t ragged = int64_t(d.in_bits >> 48);
+        double lo = 0.0;                     // SUMSQ: this lane's sum of lo parts
+        uint64_t hib = 0;                    // SUMSQ: sum of bits(t) - bits(C)
         if (ragged == 0 && (d.out_bits & 1) == 0) {
             g_cu32x2 *src = (g_cu32x2 *)in;
             g_f32x4 *dst = (g_f32x4 *)out;
             u32x2 v[kUnscaleUnroll];
 #pragma unroll
             for (int u = 0; u < kUnscaleUnroll; ++u) v[u] = src[u * kUnscaleThreads + tid];
+            if (SUMSQ) hib = uint64_t(0) - uint64_t(kUnscaleUnroll * kUnscaleVec) * kSplitBits;
 #pragma unroll
             for (int u = 0; u < kUnscaleUnroll; ++u) {
-                const f32x4 y = {unscale_one(v[u].x & 0xFFFFu, inv, bad),
-                                 unscale_one(v[u].x >> 16, inv, bad),
-                                 unscale_one(v[u].y & 0xFFFFu, inv, bad),
-                                 unscale_one(v[u].y >> 16, inv, bad)};
+                const float f0 = widen_f16(v[u].x & 0xFFFFu), f1 = widen_f16(v[u].x >> 16);
+                const float f2 = widen_f16(v[u].y & 0xFFFFu), f3 = widen_f16(v[u].y >> 16);
+                const f32x4 y = {unscale_f(f0, inv, bad), unscale_f(f1, inv, bad),
+                                 unscale_f(f2, inv, bad), unscale_f(f3, inv, bad)};
                 __builtin_nontemporal_store(y, &dst[u * kUnscaleThreads + tid]);
+                if (SUMSQ) {
+                    sq_add(f0, lo, hib);
+                    sq_add(f1, lo, hib);
+                    sq_add(f2, lo, hib);
+                    sq_add(f3, lo, hib);
+                }
+            }
+            // A non-finite input makes lo NaN; redo this lane's share with
+            // Inf and NaN replaced by 0 (which adds t = C, i.e. hi = lo = 0).
+            if (SUMSQ && !__builtin_isfinite(lo)) {
+                lo = 0.0;
+                hib = uint64_t(0) - uint64_t(kUnscaleUnroll * kUnscaleVec) * kSplitBits;
+#pragma unroll
+                for (int u = 0; u < kUnscaleUnroll; ++u) {
+                    const uint32_t w[2] = {v[u].x, v[u].y};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float f = widen_f16((w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+                        sq_add(__builtin_isfinite(f) ? f : 0.0f, lo, hib);
+                    }
+                }
             }
         } else {
             const int64_t cnt = ragged ? ragged : kUnscaleChunk;
-            for (int64_t i = tid; i < cnt; i += kUnscaleThreads) out[i] = unscale_one(in[i], inv, bad);
+            for (int64_t i = tid; i < cnt; i += kUnscaleThreads) {
+                const float f = widen_f16(in[i]);
+                out[i] = unscale_f(f, inv, bad);
+                if (SUMSQ && __builtin_isfinite(f)) {
+                    sq_add(f, lo, hib);
+                    hib -= kSplitBits;
+                }
+            }
+        }
+        if (SUMSQ) {
+            // lo * 2^48 is an integer of magnitude <= 2^32: read it off the
+            // bits of lo * 2^48 + 1.5 * 2^52 (exact).
+            const double m = lo * 0x1p48 + kIntMagic;
+            uint64_t a = (uint64_t)__double_as_longlong(m) - kIntMagicBits;
+            uint64_t b = hib;
+            a = row_sum_u64(a);
+            b = row_sum_u64(b);
+            if ((tid & 15) == 0) {
+                red[0][tid >> 4] = b;
+                red[1][tid >> 4] = a;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                uint64_t sb = 0, sa = 0;
+#pragma unroll
+                for (int w = 0; w < kUnscaleThreads / 16; ++w) {
+                    sb += red[0][w];
+                    sa += red[1][w];
+                }
+                parts[c] = u64x2{sb, sa};     // chunk sum = sb * 2^30 + (int64)sa
+            }
+            __syncthreads();
         }
     }
     if (bad) *found_inf = 1;                 // idempotent; only ever 1
+}
+
+// 128-bit running sums as (lo, hi) word pairs
+__device__ __forceinline__ void add128(uint64_t &lo, uint64_t &hi, uint64_t blo, uint64_t bhi) {
+    lo += blo;
+    hi += bhi + (lo < blo ? 1u : 0u);
+}
+
+// Sum of the 128-bit values (lo[i], hi[i]) of a workgroup's threads; the
+// result is valid in thread 0.
+template <int T>
+__device__ __forceinline__ void block_sum128(uint64_t &lo, uint64_t &hi) {
+    __shared__ uint64_t slo[T], shi[T];
+    const int tid = threadIdx.x;
+    slo[tid] = lo;
+    shi[tid] = hi;
+    __syncthreads();
+#pragma unroll
+    for (int s = T / 2; s > 0; s >>= 1) {
+        if (tid < s) {
+            uint64_t l = slo[tid], h = shi[tid];
+            add128(l, h, slo[tid + s], shi[tid + s]);
+            slo[tid] = l;
+            shi[tid] = h;
+        }
+        __syncthreads();
+    }
+    lo = slo[0];
+    hi = shi[0];
+}
+
+constexpr int kSumsqThreads = 256;
+
+// Second level: each workgroup adds a strided share of the chunk partials
+// (X = B * 2^30 + A, A signed) into one 128-bit value.
+__global__ __launch_bounds__(kSumsqThreads)
+void sumsq_reduce_kernel(const u64x2 *__restrict__ parts, int64_t nparts,
+                         u64x2 *__restrict__ level2) {
+    uint64_t lo = 0, hi = 0;
+    for (int64_t i = int64_t(blockIdx.x) * kSumsqThreads + threadIdx.x; i < nparts;
+         i += int64_t(gridDim.x) * kSumsqThreads) {
+        const u64x2 p = parts[i];
+        add128(lo, hi, p.x << 30, p.x >> 34);
+        add128(lo, hi, p.y, (int64_t)p.y < 0 ? ~uint64_t(0) : uint64_t(0));
+    }
+    block_sum128<kSumsqThreads>(lo, hi);
+    if (threadIdx.x == 0) level2[blockIdx.x] = u64x2{lo, hi};
+}
+
+// Round-to-nearest-even conversion of the 128-bit integer hi * 2^64 + lo.
+__device__ double u128_to_f64(uint64_t hi, uint64_t lo) {
+    uint64_t m, sticky;
+    int sh;                                  // value = (m + f) * 2^sh, 0 <= f < 1, sticky = f != 0
+    if (hi == 0) {
+        m = lo;
+        sticky = 0;
+        sh = 0;
+    } else {
+        const int hb = 64 - __clzll((long long)hi);    // 1..64
+        if (hb == 64) {
+            m = hi;
+            sticky = lo != 0;
+        } else {
+            m = (hi << (64 - hb)) | (lo >> hb);
+            sticky = (lo << (64 - hb)) != 0;
+        }
+        sh = hb;
+    }
+    if (m < (uint64_t(1) << 53)) return ldexp((double)m, sh);   // exact (sticky is 0 here)
+    const int drop = 11 - __clzll((long long)m);                  // keep 53 bits
+    uint64_t keep = m >> drop;
+    const uint64_t rem = m & ((uint64_t(1) << drop) - 1);
+    const uint64_t half = uint64_t(1) << (drop - 1);
+    if (rem > half || (rem == half && (sticky || (keep & 1)))) keep += 1;
+    return ldexp((double)keep, sh + drop);                        // keep <= 2^53: exact
+}
+
+// Final: add the second-level values to the running total sumsq[0] +
+// sumsq[1] * 2^64 and write norm_sq = (fl64(total) * 2^-48) * (inv * inv).
+__global__ __launch_bounds__(kSumsqThreads)
+void sumsq_final_kernel(const u64x2 *__restrict__ level2, int32_t n2,
+                        const float *__restrict__ scale, uint64_t *__restrict__ sumsq,
+                        double *__restrict__ norm_sq) {
+    uint64_t lo = 0, hi = 0;
+    for (int i = threadIdx.x; i < n2; i += kSumsqThreads) add128(lo, hi, level2[i].x, level2[i].y);
+    block_sum128<kSumsqThreads>(lo, hi);
+    if (threadIdx.x == 0) {
+        add128(lo, hi, sumsq[0], sumsq[1]);
+        sumsq[0] = lo;
+        sumsq[1] = hi;
+        const float inv = 1.0f / *scale;
+        const double i2 = (double)inv * (double)inv;             // exact
+        *norm_sq = (u128_to_f64(hi, lo) * 0x1p-48) * i2;
+    }
 }
 
 __global__ void update_scale_kernel(float *scale, int32_t *tracker, int32_t *found_inf,
@@ -114,8 +309,35 @@ hipError_t launch_unscale_check(const ChunkDesc *descs, int64_t nchunks, const f
     if (nchunks <= 0) return hipSuccess;
     const int64_t cap = GS_UNSCALE_GRID_CAP;
     const int64_t grid = nchunks < cap ? nchunks : cap;
-    hipLaunchKernelGGL(unscale_check_kernel, dim3((uint32_t)grid), dim3(kUnscaleThreads), 0,
-                       stream, descs, nchunks, scale, found_inf);
+    hipLaunchKernelGGL(unscale_check_kernel<false>, dim3((uint32_t)grid), dim3(kUnscaleThreads),
+                       0, stream, descs, nchunks, scale, found_inf, (u64x2 *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_unscale_check_sumsq(const ChunkDesc *descs, int64_t nchunks, const float *scale,
+                                      int32_t *found_inf, uint64_t *sumsq, double *norm_sq,
+                                      void *workspace, hipStream_t stream) {
+    u64x2 *parts = static_cast<u64x2 *>(workspace);
+    u64x2 *level2 = parts + nchunks;
+    int32_t n2 = 0;
+    if (nchunks > 0) {
+        const int64_t cap = GS_UNSCALE_GRID_CAP;
+        const int64_t grid = nchunks < cap ? nchunks : cap;
+        hipLaunchKernelGGL(unscale_check_kernel<true>, dim3((uint32_t)grid),
+                           dim3(kUnscaleThreads), 0, stream, descs, nchunks, scale, found_inf,
+                           parts);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // about 8 or more partials per second-level thread
+        const int64_t want = (nchunks + 8 * kSumsqThreads - 1) / (8 * kSumsqThreads);
+        n2 = int32_t(want < kSumsqL2 ? want : kSumsqL2);
+        hipLaunchKernelGGL(sumsq_reduce_kernel, dim3((uint32_t)n2), dim3(kSumsqThreads), 0,
+                           stream, parts, nchunks, level2);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(kSumsqThreads), 0, stream, level2, n2,
+                       scale, sumsq, norm_sq);
     return hipGetLastError();
 }
 

@@ -143,3 +143,35 @@ def test_quantize_delayed_argument_errors():
     assert call(pos=FAKE + 2) == -6
     assert call(ws=None) == -7
     assert call(wsb=100) == -7
+
+
+def test_unscale_sumsq_workspace_size():
+    assert gs.gs_unscale_check_sumsq_workspace_size([]) == 16 * 1024
+    assert gs.gs_unscale_check_sumsq_workspace_size([1, 2048, 2049, 0]) == 16 * (1 + 1 + 2 + 1024)
+    assert gs.gs_unscale_check_sumsq_workspace_size([-1]) == 0
+
+
+def test_unscale_sumsq_argument_errors():
+    L = gs.lib()
+    f = L.gs_unscale_check_sumsq
+    one = (ctypes.c_void_p * 1)(FAKE)
+    n5 = (ctypes.c_int64 * 1)(5)
+    ws = 16 * 1025
+    args = dict(n=1, g=one, o=one, nums=n5, dt=gs.GS_F16, s=FAKE, fi=FAKE, sq=FAKE, ns=FAKE,
+                ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["n"], a["g"], a["o"], a["nums"], a["dt"], a["s"], a["fi"], a["sq"], a["ns"],
+                 a["ws"], a["wsb"], None)
+    assert call(n=-1) == -2
+    assert call(dt=gs.GS_BF16) == -4
+    for k in ("s", "fi", "sq", "ns", "g", "o", "nums"):
+        assert call(**{k: None}) == -1, k
+    assert call(nums=(ctypes.c_int64 * 1)(-3)) == -2
+    assert call(sq=FAKE + 4) == -6
+    assert call(ns=FAKE + 4) == -6
+    assert call(g=(ctypes.c_void_p * 1)(FAKE + 1)) == -6
+    assert call(ws=None) == -7
+    assert call(wsb=ws - 1) == -7
+    assert call(ws=FAKE + 8) == -6
