@@ -55,6 +55,12 @@ PINS = {
     "unscale_check_sumsq": "exact integer sum of squares against Python integers; "
                            "norm_sq against numpy float64 sums within 1e-12",
     "update_scale": "page 5-step trace; closed-form trajectories (collapse, overflow, C1)",
+    "update_scale_hysteresis": "reduces to the pinned GradScaler policy (hysteresis 1, no "
+                               "floor) on random flag sequences; closed-form trajectories "
+                               "(floor, budget spent and refilled, growth every window); the "
+                               "page's comparison of the two policies (growth twice as eager, "
+                               "different skip rate from the same start); the knob semantics "
+                               "are a reading of their names",
     "quantize": "page fp8_scaling.py listing run by torch CPU; page error table; "
                 "outlier exercise; scale-invariance and error-bound properties",
     "dequantize": "page quant() listing run by torch CPU",
@@ -101,6 +107,8 @@ def lib() -> ctypes.CDLL:
             L.orc_unscale_check_sumsq.restype = None
             L.orc_update_scale.argtypes = [P, P, P, F, F, I32, P]
             L.orc_update_scale.restype = None
+            L.orc_update_scale_hysteresis.argtypes = [P, P, P, P, F, F, I32, I32, I32, F, P]
+            L.orc_update_scale_hysteresis.restype = None
             L.orc_block_amax.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, I64]
             L.orc_block_amax.restype = F
             L.orc_scale_from_amax.argtypes = [F, ctypes.c_int]
@@ -243,6 +251,24 @@ def update_scale(st: ScalerState, growth: float = 2.0, backoff: float = 0.5,
     lib().orc_update_scale(ctypes.byref(st.scale), ctypes.byref(st.tracker),
                            ctypes.byref(st.found_inf), float(growth), float(backoff),
                            int(interval), ctypes.byref(st.skips))
+
+
+class HysteresisState(ScalerState):
+    """ScalerState plus the hysteresis budget h (start it at H)."""
+
+    def __init__(self, scale: float = 65536.0, tracker: int = 0, h: int = 2):
+        super().__init__(scale, tracker)
+        self.h = ctypes.c_int32(h)
+
+
+def update_scale_hysteresis(st: HysteresisState, growth: float = 2.0, backoff: float = 0.5,
+                            window: int = 1000, hysteresis: int = 2, consecutive: bool = False,
+                            min_scale: float = 1.0) -> None:
+    lib().orc_update_scale_hysteresis(ctypes.byref(st.scale), ctypes.byref(st.tracker),
+                                      ctypes.byref(st.h), ctypes.byref(st.found_inf),
+                                      float(growth), float(backoff), int(window), int(hysteresis),
+                                      int(bool(consecutive)), float(min_scale),
+                                      ctypes.byref(st.skips))
 
 
 # ---------------------------------------------------------------- quantize

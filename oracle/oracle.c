@@ -267,6 +267,52 @@ void orc_update_scale(float *S, int32_t *tracker, int32_t *found_inf,
     *found_inf = 0;
 }
 
+/* The second scaler policy of [NP]'s loss-scaler constants paragraph (the
+ * DeepSpeed fp16 block): start 2^16, window 1000, hysteresis 2,
+ * consecutive_hysteresis false, min_loss_scale 1.  The page names these
+ * knobs without defining them; the plainest reading of each name:
+ *   overflow step: skipped (skips += 1); the clean-step count restarts
+ *                  (tracker = 0); if the hysteresis budget h is spent
+ *                  (h <= 1) the scale is lowered,
+ *                  S = max(fl32(S * backoff), min_scale),
+ *                  otherwise one unit of budget is spent (h -= 1) and S
+ *                  is kept;
+ *   clean step:    with consecutive hysteresis the budget refills (h = H),
+ *                  so only H overflows in a row lower S; then
+ *                  tracker += 1 and when tracker >= window,
+ *                  S = fl32(S * growth), tracker = 0 and, without
+ *                  consecutive hysteresis, the budget refills there.
+ *   The flag is consumed.  With H = 1 and min_scale = 0 this is exactly
+ *   orc_update_scale (the GradScaler policy). */
+void orc_update_scale_hysteresis(float *S, int32_t *tracker, int32_t *h,
+                                 int32_t *found_inf, float growth, float backoff,
+                                 int32_t window, int32_t H, int32_t consecutive,
+                                 float min_scale, int64_t *skips)
+{
+    if (*found_inf) {
+        if (skips)
+            *skips += 1;
+        *tracker = 0;
+        if (*h <= 1) {
+            float lowered = *S * backoff;
+            *S = lowered > min_scale ? lowered : min_scale;
+        } else {
+            *h -= 1;
+        }
+    } else {
+        if (consecutive)
+            *h = H;
+        *tracker += 1;
+        if (*tracker >= window) {
+            *S = *S * growth;
+            *tracker = 0;
+            if (!consecutive)
+                *h = H;
+        }
+    }
+    *found_inf = 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* FP8 scaled quantization, [MP] per_tensor / per_block / quant and [WHY]
  * Failure 1 and "The seam".  Input rows x cols row-major, BF16 or FP32,

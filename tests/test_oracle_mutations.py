@@ -29,7 +29,8 @@ MUTANTS = {
     "no_canonical_nan": ("o[i] = f32_of_bits(CANONICAL_NAN);", "o[i] = y;"),
     "growth_strict_gt": ("if (*tracker >= interval)", "if (*tracker > interval)"),
     "tracker_kept_on_skip": ("*tracker = 0;\n        if (skips)", "if (skips)"),
-    "flag_not_cleared": ("    *found_inf = 0;\n}", "}"),
+    "flag_not_cleared": ("            *tracker = 0;\n        }\n    }\n    *found_inf = 0;\n}",
+                         "            *tracker = 0;\n        }\n    }\n}"),
     "amax_counts_inf": ("if (isfinite(f) && fabsf(f) > amax)", "if (!isnan(f) && fabsf(f) > amax)"),
     "no_floor": ("float a = amax > floor_ ? amax : floor_;", "float a = amax; (void)floor_;"),
     "scale_inverted": ("return a / (float)fmt_max(fmt);", "return (float)fmt_max(fmt) / a;"),
@@ -41,12 +42,20 @@ MUTANTS = {
     "sumsq_wrong_unit": ("uint64_t G = (uint64_t)(fabs(g) * 16777216.0);", "uint64_t G = (uint64_t)(fabs(g) * 8388608.0);"),
     "sumsq_not_accumulated": ("    total += X;", "    total = X;"),
     "norm_without_inverse": ("*norm_sq = (d * 0x1p-48) * ((double)inv * (double)inv);", "*norm_sq = (d * 0x1p-48);"),
+    "hyst_consecutive_inverted": ("        if (consecutive)\n            *h = H;",
+                                  "        if (!consecutive)\n            *h = H;"),
+    "hyst_no_min_scale": ("*S = lowered > min_scale ? lowered : min_scale;", "*S = lowered;"),
+    "hyst_no_refill_at_growth": ("            if (!consecutive)\n                *h = H;",
+                                 "            (void)consecutive;"),
+    "hyst_budget_off_by_one": ("if (*h <= 1) {", "if (*h <= 0) {"),
+    "hyst_window_not_restarted": ("        *tracker = 0;\n        if (*h <= 1) {",
+                                  "        if (*h <= 1) {"),
     "nan_input_unsigned": ("return (uint8_t)((signbit(f) ? 0x80 : 0x00) | 0x7F);", "return 0x7F;"),
 }
 
 FAST_PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_unscale.py",
              "tests/test_oracle_quant.py", "tests/test_oracle_delayed.py",
-             "tests/test_oracle_sumsq.py"]
+             "tests/test_oracle_sumsq.py", "tests/test_oracle_hysteresis.py"]
 
 
 def _run_mutant(name, tmp_dir):
