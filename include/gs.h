@@ -156,6 +156,42 @@ gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_
                           int64_t *skip_count, void *stream);
 
 /*
+ * gs_update_scale_hysteresis -- the second loss-scaler policy of "Numerical
+ * Precision, Mixed Precision, and Loss Scaling" (loss-scaler constants
+ * paragraph: the DeepSpeed fp16 block, start 2^16, loss_scale_window 1000,
+ * hysteresis 2, consecutive_hysteresis false, min_loss_scale 1).  The page
+ * names the knobs; their meaning here is the plain reading of the names:
+ *   if *found_inf != 0:  *skip_count += 1 (when not NULL); *growth_tracker = 0;
+ *                        if *hysteresis_left <= 1:
+ *                            S = max(fl32(S * backoff_factor), min_scale)
+ *                        else *hysteresis_left -= 1 (S kept)
+ *   else:                if consecutive_hysteresis, *hysteresis_left = hysteresis;
+ *                        *growth_tracker += 1; when it reaches growth_interval,
+ *                        S = fl32(S * growth_factor), *growth_tracker = 0 and,
+ *                        if not consecutive_hysteresis,
+ *                        *hysteresis_left = hysteresis
+ *   then *found_inf = 0.
+ * So an overflow always skips the step, but S is lowered only on the
+ * hysteresis-th overflow since the budget was last refilled (only
+ * consecutive ones count when consecutive_hysteresis is 1), and never below
+ * min_scale.  With hysteresis 1 and min_scale 0 this is gs_update_scale.
+ *
+ *   scale, growth_tracker, hysteresis_left, found_inf: device scalars
+ *       (FP32, int32, int32, int32); start hysteresis_left at `hysteresis`.
+ *   growth_factor, backoff_factor: finite and > 0 (2.0, 0.5).
+ *   growth_interval: > 0 (the window, 1000).  hysteresis: >= 1 (2).
+ *   consecutive_hysteresis: 0 or 1 (0).  min_scale: finite, >= 0 (1.0).
+ *   skip_count: device int64 or NULL.
+ * One single-lane kernel on `stream`; no host synchronisation.
+ */
+gs_status gs_update_scale_hysteresis(float *scale, int32_t *growth_tracker,
+                                     int32_t *hysteresis_left, int32_t *found_inf,
+                                     float growth_factor, float backoff_factor,
+                                     int32_t growth_interval, int32_t hysteresis,
+                                     int32_t consecutive_hysteresis, float min_scale,
+                                     int64_t *skip_count, void *stream);
+
+/*
  * fp8_quantize_workspace_size -- bytes of device workspace fp8_quantize
  * needs for this shape and granularity in FP8_SCALE_FROM_AMAX mode: 32 KiB of
  * per-workgroup partial maxima for per-tensor scaling (the scale depends on

@@ -24,7 +24,7 @@ FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
 FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 
 EXPORTS = ("gs_unscale_check", "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
-           "gs_update_scale", "fp8_quantize_workspace_size",
+           "gs_update_scale", "gs_update_scale_hysteresis", "fp8_quantize_workspace_size",
            "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "gs_status_string")
 
 _lib = None
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.gs_unscale_check_sumsq.restype = I32
         L.gs_update_scale.argtypes = [P, P, P, F, F, I32, P, P]
         L.gs_update_scale.restype = I32
+        L.gs_update_scale_hysteresis.argtypes = [P, P, P, P, F, F, I32, I32, I32, F, P, P]
+        L.gs_update_scale_hysteresis.restype = I32
         L.fp8_quantize_workspace_size.argtypes = [I64, I64, ctypes.c_int]
         L.fp8_quantize_workspace_size.restype = ctypes.c_size_t
         L.fp8_quantize.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int,
@@ -165,6 +167,20 @@ def gs_update_scale(scale, growth_tracker, found_inf, growth_factor: float = 2.0
                                  float(growth_factor), float(backoff_factor),
                                  int(growth_interval), _ptr(skip_count), _stream(stream)),
            "gs_update_scale")
+
+
+def gs_update_scale_hysteresis(scale, growth_tracker, hysteresis_left, found_inf,
+                               growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                               growth_interval: int = 1000, hysteresis: int = 2,
+                               consecutive_hysteresis: bool = False, min_scale: float = 1.0,
+                               skip_count=None, stream=None) -> None:
+    """Update with a hysteresis budget, a floor and a growth window (defaults:
+    the DeepSpeed fp16 block's 1000 / 2 / false / 1)."""
+    _check(lib().gs_update_scale_hysteresis(
+        _ptr(scale), _ptr(growth_tracker), _ptr(hysteresis_left), _ptr(found_inf),
+        float(growth_factor), float(backoff_factor), int(growth_interval), int(hysteresis),
+        int(bool(consecutive_hysteresis)), float(min_scale), _ptr(skip_count),
+        _stream(stream)), "gs_update_scale_hysteresis")
 
 
 # ------------------------------------------------------------------ FP8

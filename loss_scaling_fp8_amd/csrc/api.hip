@@ -242,6 +242,27 @@ gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_
                                              static_cast<hipStream_t>(stream)));
 }
 
+gs_status gs_update_scale_hysteresis(float *scale, int32_t *growth_tracker,
+                                     int32_t *hysteresis_left, int32_t *found_inf,
+                                     float growth_factor, float backoff_factor,
+                                     int32_t growth_interval, int32_t hysteresis,
+                                     int32_t consecutive_hysteresis, float min_scale,
+                                     int64_t *skip_count, void *stream) {
+    if (!scale || !growth_tracker || !hysteresis_left || !found_inf) return GS_ERR_NULL;
+    if (misaligned(scale, 4) || misaligned(growth_tracker, 4) || misaligned(hysteresis_left, 4) ||
+        misaligned(found_inf, 4) || misaligned(skip_count, 8))
+        return GS_ERR_ALIGN;
+    if (!(std::isfinite(growth_factor) && growth_factor > 0.0f)) return GS_ERR_ARG;
+    if (!(std::isfinite(backoff_factor) && backoff_factor > 0.0f)) return GS_ERR_ARG;
+    if (growth_interval <= 0 || hysteresis < 1) return GS_ERR_ARG;
+    if (consecutive_hysteresis != 0 && consecutive_hysteresis != 1) return GS_ERR_ARG;
+    if (!(std::isfinite(min_scale) && min_scale >= 0.0f)) return GS_ERR_ARG;
+    return from_hip(gsk::launch_update_scale_hysteresis(
+        scale, growth_tracker, hysteresis_left, found_inf, growth_factor, backoff_factor,
+        growth_interval, hysteresis, consecutive_hysteresis, min_scale, skip_count,
+        static_cast<hipStream_t>(stream)));
+}
+
 size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g) {
     (void)rows;
     (void)cols;

@@ -41,6 +41,10 @@ constexpr size_t kSumsqPartBytes = 16;
 hipError_t launch_unscale_check_sumsq(const ChunkDesc *descs, int64_t nchunks, const float *scale,
                                       int32_t *found_inf, uint64_t *sumsq, double *norm_sq,
                                       void *workspace, hipStream_t stream);
+hipError_t launch_update_scale_hysteresis(float *scale, int32_t *tracker, int32_t *hleft,
+                                          int32_t *found_inf, float growth, float backoff,
+                                          int32_t window, int32_t hysteresis, int32_t consecutive,
+                                          float min_scale, int64_t *skips, hipStream_t stream);
 hipError_t launch_update_scale(float *scale, int32_t *tracker, int32_t *found_inf, float growth,
                                float backoff, int32_t interval, int64_t *skips,
                                hipStream_t stream);

@@ -302,7 +302,53 @@ __global__ void update_scale_kernel(float *scale, int32_t *tracker, int32_t *fou
     *found_inf = 0;
 }
 
+// The same update with a hysteresis budget h, a floor on S and a growth
+// window: an overflow restarts the window and either lowers S (budget spent:
+// S = max(fl32(S * backoff), min_scale)) or spends one unit of budget; a
+// clean step refills the budget when `consecutive`, and a growth refills it
+// otherwise.
+__global__ void update_scale_hysteresis_kernel(float *scale, int32_t *tracker, int32_t *hleft,
+                                               int32_t *found_inf, float growth, float backoff,
+                                               int32_t window, int32_t H, int32_t consecutive,
+                                               float min_scale, int64_t *skips) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    float S = *scale;
+    int32_t t = *tracker, h = *hleft;
+    if (*found_inf) {
+        if (skips) *skips = *skips + 1;
+        t = 0;
+        if (h <= 1) {
+            const float lowered = S * backoff;
+            S = lowered > min_scale ? lowered : min_scale;
+        } else {
+            h -= 1;
+        }
+    } else {
+        if (consecutive) h = H;
+        t += 1;
+        if (t >= window) {
+            S = S * growth;
+            t = 0;
+            if (!consecutive) h = H;
+        }
+    }
+    *scale = S;
+    *tracker = t;
+    *hleft = h;
+    *found_inf = 0;
+}
+
 }  // namespace
+
+hipError_t launch_update_scale_hysteresis(float *scale, int32_t *tracker, int32_t *hleft,
+                                          int32_t *found_inf, float growth, float backoff,
+                                          int32_t window, int32_t hysteresis, int32_t consecutive,
+                                          float min_scale, int64_t *skips, hipStream_t stream) {
+    hipLaunchKernelGGL(update_scale_hysteresis_kernel, dim3(1), dim3(64), 0, stream, scale,
+                       tracker, hleft, found_inf, growth, backoff, window, hysteresis,
+                       consecutive, min_scale, skips);
+    return hipGetLastError();
+}
 
 hipError_t launch_unscale_check(const ChunkDesc *descs, int64_t nchunks, const float *scale,
                                 int32_t *found_inf, hipStream_t stream) {

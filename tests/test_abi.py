@@ -175,3 +175,25 @@ def test_unscale_sumsq_argument_errors():
     assert call(ws=None) == -7
     assert call(wsb=ws - 1) == -7
     assert call(ws=FAKE + 8) == -6
+
+
+def test_update_hysteresis_argument_errors():
+    L = gs.lib()
+    f = L.gs_update_scale_hysteresis
+    args = dict(s=FAKE, t=FAKE, h=FAKE, fi=FAKE, g=2.0, b=0.5, w=1000, H=2, c=0, m=1.0, k=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["s"], a["t"], a["h"], a["fi"], a["g"], a["b"], a["w"], a["H"], a["c"], a["m"],
+                 a["k"], None)
+    for k in ("s", "t", "h", "fi"):
+        assert call(**{k: None}) == -1, k
+    assert call(h=FAKE + 2) == -6
+    assert call(k=FAKE + 4) == -6
+    assert call(w=0) == -5
+    assert call(H=0) == -5
+    assert call(c=2) == -5
+    assert call(m=-1.0) == -5
+    assert call(m=float("nan")) == -5
+    assert call(g=float("inf")) == -5
+    assert call(b=0.0) == -5
