@@ -40,7 +40,7 @@ _CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
 
 F16, BF16, F32 = 1, 2, 3
 E4M3, E5M2 = 0, 1
-PER_TENSOR, BLOCK_1x128, BLOCK_128x128 = 0, 1, 2
+PER_TENSOR, BLOCK_1x128, BLOCK_128x128, BLOCK_1x32 = 0, 1, 2, 3
 FROM_AMAX, GIVEN = 0, 1
 FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
 CANONICAL_NAN_BITS = 0x7FC00000
@@ -64,6 +64,10 @@ PINS = {
     "quantize": "page fp8_scaling.py listing run by torch CPU; page error table; "
                 "outlier exercise; scale-invariance and error-bound properties",
     "dequantize": "page quant() listing run by torch CPU",
+    "quantize_mx": "the page's listing with 1x32 blocks run by torch CPU, its scale rounded "
+                   "up to a power of two by torch.frexp (the E8M0 reading); the scale is the "
+                   "exponent field; no saturation; power-of-two invariance",
+    "dequantize_mx": "torch float8 decode times torch.ldexp of the byte, NaN byte",
     "quantize_delayed": "reduces to the pinned per-tensor quantizer (history 1, same "
                         "tensor twice); window max closed form; the pages' spike failure "
                         "shape (saturation); otherwise parity unpinned",
@@ -122,6 +126,10 @@ def lib() -> ctypes.CDLL:
                                                I32, P, P, P, P]
             L.orc_quantize_delayed.restype = ctypes.c_int
             L.orc_dequantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P]
+            L.orc_quantize_mx.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, P, P, P]
+            L.orc_quantize_mx.restype = ctypes.c_int
+            L.orc_dequantize_mx.argtypes = [P, I64, I64, ctypes.c_int, P, P]
+            L.orc_dequantize_mx.restype = ctypes.c_int
             L.orc_dequantize.restype = ctypes.c_int
             L.orc_fp8_encode_array.argtypes = [P, I64, ctypes.c_int, P]
             L.orc_fp8_encode_array.restype = None
@@ -285,6 +293,8 @@ def n_scales(rows: int, cols: int, gran: int) -> int:
         return 1
     if gran == BLOCK_1x128:
         return rows * (cols // 128)
+    if gran == BLOCK_1x32:
+        return rows * (cols // 32)
     return (rows // 128) * (cols // 128)
 
 
@@ -336,6 +346,30 @@ def quantize_delayed(x: np.ndarray, fmt: int, st: DelayedState):
     if rc != 0:
         raise ValueError("bad delayed-scaling state")
     return codes, used[0], nf.value
+
+
+def quantize_mx(x: np.ndarray, fmt: int):
+    """MX-style 1x32 blocks with E8M0 power-of-two scales: returns (codes
+    uint8 [rows, cols], scales uint8 [rows, cols/32], nonfinite)."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, max(cols // 32, 1)), np.uint8)
+    nf = ctypes.c_int32(0)
+    if lib().orc_quantize_mx(_ptr(x), dt, rows, cols, fmt, _ptr(codes), _ptr(sc),
+                             ctypes.byref(nf)) != 0:
+        raise ValueError("cols must be a multiple of 32")
+    return codes, sc[:, :cols // 32], nf.value
+
+
+def dequantize_mx(codes: np.ndarray, fmt: int, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    rows, cols = codes.shape
+    sc = np.ascontiguousarray(scales, np.uint8)
+    out = np.empty((rows, cols), np.float32)
+    if lib().orc_dequantize_mx(_ptr(codes), rows, cols, fmt, _ptr(sc), _ptr(out)) != 0:
+        raise ValueError("cols must be a multiple of 32")
+    return out
 
 
 def dequantize(codes: np.ndarray, fmt: int, gran: int, scales: np.ndarray) -> np.ndarray:

@@ -33,7 +33,10 @@
  *   [MP]  "Mixed precision and FP8 training": section "FP8 training", the
  *         fp8_scaling.py listing (quant: divide, clamp to +-MAX, cast to FP8,
  *         cast back and multiply by the scale; per_tensor; per_block with the
- *         1e-12 floor on the block max-abs).
+ *         1e-12 floor on the block max-abs), and the hardware notes (MX
+ *         formats: one scaling factor per 32 elements).
+ *   [LS-d] "Loss Scaling" (glossary page), "Where it fits": loss scaling
+ *         pairs with gradient clipping.
  *
  * Readings taken where the pages are silent (each is a definition here):
  *   - the unscale multiplies by inv = fl32(1/S) computed once;
@@ -42,7 +45,13 @@
  *   - block max-abs ignores NaN and +-Inf (finite-only amax);
  *   - the 1e-12 floor applies at every granularity;
  *   - a NaN input encodes as sign|0x7F, any other NaN quotient as 0x7F;
- *   - the sign of zero is kept (-0 and negative underflow give 0x80).
+ *   - the sign of zero is kept (-0 and negative underflow give 0x80);
+ *   - delayed scaling derives s from the maximum over the amax window;
+ *   - the gradient norm is the exact sum of squares of the finite inputs;
+ *   - the second scaler policy's knobs mean what their names say (budget
+ *     of H overflows, refilled by clean steps or by growth; floor on S);
+ *   - MX-style blocks are 1x32 along a row with a power-of-two (E8M0)
+ *     scale, the smallest not below the pages' block scale.
  * Parity unpinned: these reading-defined rules (finite-only amax, NaN
  * canonicalisation, the floor at per-tensor granularity, the set-only flag
  * and the skip count) have no value on the pages to check against; they are
@@ -57,7 +66,7 @@
 /* Enumerations (same numeric values as the public ABI, restated here). */
 enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_F32 = 3 };
 enum { ORC_E4M3 = 0, ORC_E5M2 = 1 };
-enum { ORC_PER_TENSOR = 0, ORC_BLOCK_1x128 = 1, ORC_BLOCK_128x128 = 2 };
+enum { ORC_PER_TENSOR = 0, ORC_BLOCK_1x128 = 1, ORC_BLOCK_128x128 = 2, ORC_BLOCK_1x32 = 3 };
 enum { ORC_FROM_AMAX = 0, ORC_GIVEN = 1 };
 
 /* ------------------------------------------------------------------ */
@@ -368,6 +377,7 @@ static void block_shape(int gran, int64_t rows, int64_t cols,
 {
     if (gran == ORC_PER_TENSOR) { *br = rows; *bc = cols; }
     else if (gran == ORC_BLOCK_1x128) { *br = 1; *bc = 128; }
+    else if (gran == ORC_BLOCK_1x32) { *br = 1; *bc = 32; }
     else { *br = 128; *bc = 128; }
 }
 
@@ -458,6 +468,64 @@ int orc_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
             int64_t b = (gran == ORC_PER_TENSOR) ? 0 : (r / br) * nbc + c / bc;
             float v = (float)orc_fp8_decode(codes[r * cols + c], fmt);
             float o = v * scales[b];
+            out[r * cols + c] = isnan(o) ? f32_of_bits(CANONICAL_NAN) : o;
+        }
+    return 0;
+}
+
+/* MX-style blocks ("Mixed precision and FP8 training", hardware notes: MX
+ * formats keep one scaling factor per 32 elements).  The pages do not say
+ * how that factor is encoded; the reading here: blocks are 1x32 along a
+ * row; the scale is a power of two stored as one E8M0 byte (2^(byte-127),
+ * 0xFF = NaN), namely the smallest power of two not below the pages' own
+ * block scale fl32(max(amax, 1e-12) / MAX), so that, as with that scale,
+ * no finite element saturates; the cast is the same divide, clamp and
+ * round-to-nearest-even.  Returns -1 when cols is not a multiple of 32. */
+static float pow2_at_least(float s)           /* s positive, normal */
+{
+    int e;
+    double m = frexp((double)s, &e);          /* s = m * 2^e, 0.5 <= m < 1 */
+    return (float)(m == 0.5 ? ldexp(1.0, e - 1) : ldexp(1.0, e));
+}
+
+int orc_quantize_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
+                    uint8_t *codes, uint8_t *scales_e8m0, int32_t *nonfinite)
+{
+    if (cols % 32 != 0)
+        return -1;
+    int any_nonfinite = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t bj = 0; bj < cols / 32; ++bj) {
+            float s = pow2_at_least(orc_scale_from_amax(
+                orc_block_amax(x, dtype, cols, r, 1, bj * 32, 32), fmt));
+            int e;
+            frexp((double)s, &e);
+            scales_e8m0[r * (cols / 32) + bj] = (uint8_t)(e - 1 + 127);   /* s = 2^(e-1) */
+            for (int64_t c = bj * 32; c < bj * 32 + 32; ++c) {
+                float f = load_elem(x, dtype, r * cols + c);
+                if (!isfinite(f))
+                    any_nonfinite = 1;
+                codes[r * cols + c] = orc_cast(f, s, fmt);
+            }
+        }
+    if (any_nonfinite && nonfinite)
+        *nonfinite = 1;
+    return 0;
+}
+
+/* out = fl32(decode(code) * 2^(byte - 127)), canonical NaN; byte 0xFF is a
+ * NaN scale. */
+int orc_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
+                      const uint8_t *scales_e8m0, float *out)
+{
+    if (cols % 32 != 0)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t b = scales_e8m0[r * (cols / 32) + c / 32];
+            float s = b == 0xFF ? f32_of_bits(CANONICAL_NAN) : (float)ldexp(1.0, (int)b - 127);
+            float v = (float)orc_fp8_decode(codes[r * cols + c], fmt);
+            float o = v * s;
             out[r * cols + c] = isnan(o) ? f32_of_bits(CANONICAL_NAN) : o;
         }
     return 0;

@@ -50,12 +50,18 @@ MUTANTS = {
     "hyst_budget_off_by_one": ("if (*h <= 1) {", "if (*h <= 0) {"),
     "hyst_window_not_restarted": ("        *tracker = 0;\n        if (*h <= 1) {",
                                   "        if (*h <= 1) {"),
+    "mx_scale_rounded_down": ("return (float)(m == 0.5 ? ldexp(1.0, e - 1) : ldexp(1.0, e));",
+                              "return (float)ldexp(1.0, e - 1);"),
+    "mx_byte_bias_128": ("(uint8_t)(e - 1 + 127)", "(uint8_t)(e - 1 + 128)"),
+    "block_1x32_as_1x64": ("{ *br = 1; *bc = 32; }", "{ *br = 1; *bc = 64; }"),
+    "mx_nan_byte_ignored": ("b == 0xFF ? f32_of_bits(CANONICAL_NAN) : ", ""),
     "nan_input_unsigned": ("return (uint8_t)((signbit(f) ? 0x80 : 0x00) | 0x7F);", "return 0x7F;"),
 }
 
 FAST_PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_unscale.py",
              "tests/test_oracle_quant.py", "tests/test_oracle_delayed.py",
-             "tests/test_oracle_sumsq.py", "tests/test_oracle_hysteresis.py"]
+             "tests/test_oracle_sumsq.py", "tests/test_oracle_hysteresis.py",
+             "tests/test_oracle_mx.py"]
 
 
 def _run_mutant(name, tmp_dir):

@@ -15,9 +15,9 @@ import oracle
 from conftest import load_golden
 
 E4M3, E5M2 = oracle.E4M3, oracle.E5M2
-PT, B1, B128 = oracle.PER_TENSOR, oracle.BLOCK_1x128, oracle.BLOCK_128x128
+PT, B1, B128, B32 = oracle.PER_TENSOR, oracle.BLOCK_1x128, oracle.BLOCK_128x128, oracle.BLOCK_1x32
 TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
-BLOCK = {PT: None, B1: (1, 128), B128: (128, 128)}
+BLOCK = {PT: None, B1: (1, 128), B128: (128, 128), B32: (1, 32)}
 
 
 def _floats(s):
@@ -54,7 +54,7 @@ def _bf16_bits(x: torch.Tensor) -> np.ndarray:
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
-@pytest.mark.parametrize("gran", [PT, B1, B128])
+@pytest.mark.parametrize("gran", [PT, B1, B128, B32])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quantize_matches_page_listing(fmt, gran, dtype):
     g = torch.Generator().manual_seed(100 + 10 * fmt + gran)
@@ -114,7 +114,7 @@ def test_page_outlier_exercise():
 
 # ---------------------------------------------------------------- properties
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
-@pytest.mark.parametrize("gran", [PT, B1, B128])
+@pytest.mark.parametrize("gran", [PT, B1, B128, B32])
 def test_scale_invariance_power_of_two(fmt, gran):
     rng = np.random.default_rng(11)
     x = (rng.standard_normal((256, 256)) * 3).astype(np.float32)
