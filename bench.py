@@ -388,6 +388,46 @@ def main():
         log("unscale+sumsq: %.3f ms (%.0f GB/s)" % (ms_sq, gbps))
         del ws
 
+    # 1x32 blocks (FP32 scales, and MX-style E8M0 scales) on the activation
+    # shape, outside the timed step, with the 1x128 pair timed the same way
+    # for reference.  Before each timed launch a 1 GiB write and a 1 GiB read
+    # (synchronised) leave the infinity cache holding clean lines of other
+    # buffers: cold inputs, and no write-back of an unrelated kernel's dirty
+    # lines charged to the launch.
+    if not args.pmc_safe:
+        junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+        def flush():
+            junk.fill_(1.0)
+            torch.cuda.synchronize()
+            junk_rd.sum()
+            torch.cuda.synchronize()
+        s32 = torch.empty(gs.scale_shape(act.rows, act.cols, gs.FP8_BLOCK_1x32),
+                          dtype=torch.float32, device=dev)
+        smx = torch.empty((act.rows, act.cols // 32), dtype=torch.uint8, device=dev)
+        nb32, nb128 = n_a // 32, n_a // 128
+        for name, fn, nbytes in (
+                ("quant_1x128_cold", lambda: gs.fp8_quantize(xa, act.fmt, act.gran, 0, ca, sa),
+                 n_a * 3 + nb128 * 4),
+                ("dequant_1x128_cold", lambda: gs.fp8_dequantize(ca, act.fmt, act.gran, sa, da),
+                 n_a * 5 + nb128 * 4),
+                ("quant_1x32", lambda: gs.fp8_quantize(xa, act.fmt, gs.FP8_BLOCK_1x32, 0, ca, s32),
+                 n_a * 3 + nb32 * 4),
+                ("dequant_1x32", lambda: gs.fp8_dequantize(ca, act.fmt, gs.FP8_BLOCK_1x32, s32, da),
+                 n_a * 5 + nb32 * 4),
+                ("quant_mx_e8m0", lambda: gs.fp8_quantize_mx(xa, act.fmt, ca, smx), n_a * 3 + nb32),
+                ("dequant_mx_e8m0", lambda: gs.fp8_dequantize_mx(ca, act.fmt, smx, da),
+                 n_a * 5 + nb32)):
+            fn()
+            ms_k, _ = _time_launches(fn, 20, flush)
+            gbps = nbytes / (ms_k * 1e-3) / 1e9
+            ext[name] = {"ms": round(ms_k, 4), "bytes": nbytes, "GBps": round(gbps, 1),
+                         "frac_of_peak": round(gbps / PEAK_GBPS, 4),
+                         "workload": "%dx%d bf16 E4M3, cold (clean) infinity cache"
+                                     % (act.rows, act.cols)}
+        del junk, junk_rd, s32, smx
+
     src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp"])
     un = kernels["unscale_check"]
     roofline = {"bound": "hbm", "achieved": un["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",

@@ -30,7 +30,8 @@
  *     store x/s, multiply by s on the way out; s from the current max-abs)
  *     and "The seam" (1x128 activation tiles, 128x128 weight blocks).
  *   "Mixed precision and FP8 training" -- section "FP8 training",
- *     fp8_scaling.py (quant, per_tensor, per_block with the 1e-12 floor).
+ *     fp8_scaling.py (quant, per_tensor, per_block with the 1e-12 floor),
+ *     and the hardware notes (MX formats: one scale per 32 elements).
  */
 #ifndef GS_FP8_H
 #define GS_FP8_H
@@ -55,7 +56,9 @@ typedef int32_t gs_status;
 
 typedef enum { GS_F16 = 1, GS_BF16 = 2, GS_F32 = 3 } gs_dtype;
 typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
-typedef enum { FP8_PER_TENSOR = 0, FP8_BLOCK_1x128 = 1, FP8_BLOCK_128x128 = 2 } fp8_granularity;
+typedef enum {
+    FP8_PER_TENSOR = 0, FP8_BLOCK_1x128 = 1, FP8_BLOCK_128x128 = 2, FP8_BLOCK_1x32 = 3
+} fp8_granularity;
 typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
 
 /*
@@ -218,12 +221,14 @@ size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g
  *   x          device, row-major rows x cols, GS_BF16 or GS_F32, 16-byte
  *              aligned (GS_ERR_ALIGN otherwise).
  *   rows, cols >= 0.  FP8_BLOCK_1x128 needs cols % 128 == 0;
+ *              FP8_BLOCK_1x32 needs cols % 32 == 0;
  *              FP8_BLOCK_128x128 needs rows % 128 == 0 and cols % 128 == 0
  *              (GS_ERR_SHAPE otherwise).  Per-tensor takes any shape.
  *   codes      device uint8, rows x cols row-major, 16-byte aligned (1x128
- *              blocks run along the contiguous dimension).
+ *              and 1x32 blocks run along the contiguous dimension).
  *   scales     device FP32, one per block, row-major: [1] (per-tensor),
- *              [rows][cols/128] (1x128) or [rows/128][cols/128] (128x128).
+ *              [rows][cols/128] (1x128), [rows][cols/32] (1x32) or
+ *              [rows/128][cols/128] (128x128).
  *              Written in FROM_AMAX mode, read in GIVEN mode.  A per-tensor
  *              quantize of an empty matrix still writes scales[0].
  *   nonfinite  device int32 or NULL; set to 1 when any input is NaN or Inf
@@ -286,6 +291,39 @@ gs_status fp8_quantize_delayed(const void *x, gs_dtype x_dtype, int64_t rows, in
  */
 gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
                          fp8_granularity g, const float *scales, float *out, void *stream);
+
+/*
+ * fp8_quantize_mx -- MX-style quantization: 1x32 blocks along each row, one
+ * power-of-two scale per block stored as an E8M0 byte ("Mixed precision and
+ * FP8 training", hardware notes: the MX formats keep one scaling factor per
+ * 32 elements; the page does not define the factor's encoding).  Per block:
+ *   amax = largest finite |x| (0 if none);
+ *   s = the smallest power of two >= fl32(max(amax, fl32(1e-12)) / MAX)
+ *       (the fp8_quantize block scale rounded up, so no finite element
+ *       saturates); scales_e8m0[block] = log2(s) + 127 (the FP32 exponent
+ *       field of s);
+ *   codes as fp8_quantize with that s (divide, clamp, round to nearest
+ *   even; NaN -> sign|0x7F).
+ *   x          device BF16 or FP32 rows x cols, 16-byte aligned;
+ *              cols % 32 == 0 (GS_ERR_SHAPE otherwise).
+ *   codes      device uint8 rows x cols, 16-byte aligned.
+ *   scales_e8m0 device uint8 [rows][cols/32].
+ *   nonfinite  device int32 or NULL, set-only as in fp8_quantize.
+ * One launch on `stream`.
+ */
+gs_status fp8_quantize_mx(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                          fp8_format fmt, uint8_t *codes, uint8_t *scales_e8m0,
+                          int32_t *nonfinite, void *stream);
+
+/*
+ * fp8_dequantize_mx -- out = fl32(decode(code) * 2^(b - 127)) with b the
+ * block's E8M0 byte (b = 0xFF is a NaN scale), the canonical NaN
+ * 0x7FC00000 where that is NaN.  codes device uint8 rows x cols (16-byte
+ * aligned, cols % 32 == 0); scales_e8m0 device uint8 [rows][cols/32]; out
+ * device FP32 rows x cols (16-byte aligned).
+ */
+gs_status fp8_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
+                            const uint8_t *scales_e8m0, float *out, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *gs_status_string(gs_status status);

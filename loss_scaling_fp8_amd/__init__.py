@@ -20,12 +20,13 @@ LIB_PATH = os.path.join(_PKG, "libgsfp8.so")
 GS_OK = 0
 GS_F16, GS_BF16, GS_F32 = 1, 2, 3
 FP8_E4M3, FP8_E5M2 = 0, 1
-FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
+FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_BLOCK_1x32 = 0, 1, 2, 3
 FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 
 EXPORTS = ("gs_unscale_check", "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
            "gs_update_scale", "gs_update_scale_hysteresis", "fp8_quantize_workspace_size",
-           "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "gs_status_string")
+           "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "fp8_quantize_mx",
+           "fp8_dequantize_mx", "gs_status_string")
 
 _lib = None
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.fp8_quantize_delayed.restype = I32
         L.fp8_dequantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P]
         L.fp8_dequantize.restype = I32
+        L.fp8_quantize_mx.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, P, P, P, P]
+        L.fp8_quantize_mx.restype = I32
+        L.fp8_dequantize_mx.argtypes = [P, I64, I64, ctypes.c_int, P, P, P]
+        L.fp8_dequantize_mx.restype = I32
         L.gs_status_string.argtypes = [I32]
         L.gs_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -97,6 +102,8 @@ def n_scales(rows: int, cols: int, gran: int) -> int:
         return 1
     if gran == FP8_BLOCK_1x128:
         return rows * (cols // 128)
+    if gran == FP8_BLOCK_1x32:
+        return rows * (cols // 32)
     return (rows // 128) * (cols // 128)
 
 
@@ -105,6 +112,8 @@ def scale_shape(rows: int, cols: int, gran: int) -> tuple:
         return (1,)
     if gran == FP8_BLOCK_1x128:
         return (rows, cols // 128)
+    if gran == FP8_BLOCK_1x32:
+        return (rows, cols // 32)
     return (rows // 128, cols // 128)
 
 
@@ -258,4 +267,37 @@ def fp8_dequantize(codes, fmt: int, gran: int, scales, out=None, stream=None):
         out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
     _check(lib().fp8_dequantize(_ptr(codes), rows, cols, int(fmt), int(gran), _ptr(scales),
                                 _ptr(out), _stream(stream)), "fp8_dequantize")
+    return out
+
+
+def fp8_quantize_mx(x, fmt: int, codes=None, scales=None, nonfinite=None, stream=None):
+    """MX-style 1x32 blocks with E8M0 power-of-two scales on a 2-D
+    bfloat16/float32 CUDA tensor; returns (codes uint8 [rows, cols], scales
+    uint8 [rows, cols/32])."""
+    import torch
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    rows, cols = x.shape
+    dt = GS_BF16 if x.dtype == torch.bfloat16 else GS_F32 if x.dtype == torch.float32 else None
+    if dt is None:
+        raise TypeError("x must be bfloat16 or float32")
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_quantize_mx(_ptr(x), dt, rows, cols, int(fmt), _ptr(codes), _ptr(scales),
+                                 _ptr(nonfinite), _stream(stream)), "fp8_quantize_mx")
+    return codes, scales
+
+
+def fp8_dequantize_mx(codes, fmt: int, scales, out=None, stream=None):
+    """decode(code) * 2^(byte - 127) in float32; returns out [rows, cols]."""
+    import torch
+    if codes.dim() != 2 or codes.dtype != torch.uint8:
+        raise TypeError("codes must be a 2-D uint8 tensor")
+    rows, cols = codes.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    _check(lib().fp8_dequantize_mx(_ptr(codes), rows, cols, int(fmt), _ptr(scales), _ptr(out),
+                                   _stream(stream)), "fp8_dequantize_mx")
     return out

@@ -134,13 +134,15 @@ gs_status get_list(int32_t n, const void *const *in, float *const *out, const in
 
 inline bool bad_enum_fmt(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
 inline bool bad_enum_gran(int g) {
-    return g != FP8_PER_TENSOR && g != FP8_BLOCK_1x128 && g != FP8_BLOCK_128x128;
+    return g != FP8_PER_TENSOR && g != FP8_BLOCK_1x128 && g != FP8_BLOCK_128x128 &&
+           g != FP8_BLOCK_1x32;
 }
 
 gs_status check_shape(int64_t rows, int64_t cols, int gran) {
     if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return GS_ERR_SIZE;
     if (rows * cols > kMaxElems) return GS_ERR_SIZE;
     if (gran == FP8_BLOCK_1x128 && cols % 128 != 0) return GS_ERR_SHAPE;
+    if (gran == FP8_BLOCK_1x32 && cols % 32 != 0) return GS_ERR_SHAPE;
     if (gran == FP8_BLOCK_128x128 && (rows % 128 != 0 || cols % 128 != 0)) return GS_ERR_SHAPE;
     return GS_OK;
 }
@@ -148,6 +150,7 @@ gs_status check_shape(int64_t rows, int64_t cols, int gran) {
 int64_t num_scales(int64_t rows, int64_t cols, int gran) {
     if (gran == FP8_PER_TENSOR) return 1;
     if (gran == FP8_BLOCK_1x128) return rows * (cols / 128);
+    if (gran == FP8_BLOCK_1x32) return rows * (cols / 32);
     return (rows / 128) * (cols / 128);
 }
 
@@ -332,6 +335,32 @@ gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_f
     if (n == 0) return GS_OK;
     return from_hip(gsk::launch_dequantize(codes, rows, cols, fmt, g, scales, out,
                                            static_cast<hipStream_t>(stream)));
+}
+
+gs_status fp8_quantize_mx(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                          fp8_format fmt, uint8_t *codes, uint8_t *scales_e8m0,
+                          int32_t *nonfinite, void *stream) {
+    if (x_dtype != GS_BF16 && x_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (bad_enum_fmt(fmt)) return GS_ERR_ARG;
+    const gs_status st = check_shape(rows, cols, FP8_BLOCK_1x32);
+    if (st != GS_OK) return st;
+    if (rows * cols > 0 && (!x || !codes || !scales_e8m0)) return GS_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(nonfinite, 4)) return GS_ERR_ALIGN;
+    if (rows * cols == 0) return GS_OK;
+    return from_hip(gsk::launch_quantize_mx(x, x_dtype, rows, cols, fmt, codes, scales_e8m0,
+                                            nonfinite, static_cast<hipStream_t>(stream)));
+}
+
+gs_status fp8_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
+                            const uint8_t *scales_e8m0, float *out, void *stream) {
+    if (bad_enum_fmt(fmt)) return GS_ERR_ARG;
+    const gs_status st = check_shape(rows, cols, FP8_BLOCK_1x32);
+    if (st != GS_OK) return st;
+    if (rows * cols > 0 && (!codes || !out || !scales_e8m0)) return GS_ERR_NULL;
+    if (misaligned(codes, 16) || misaligned(out, 16)) return GS_ERR_ALIGN;
+    if (rows * cols == 0) return GS_OK;
+    return from_hip(gsk::launch_dequantize_mx(codes, rows, cols, fmt, scales_e8m0, out,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 const char *gs_status_string(gs_status status) {

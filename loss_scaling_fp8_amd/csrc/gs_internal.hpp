@@ -60,6 +60,11 @@ hipError_t launch_quantize_delayed(const void *x, gs_dtype dt, int64_t rows, int
                                    int fmt, float *scale_state, float *history, int32_t hlen,
                                    int32_t *pos, uint8_t *codes, float *scale_used,
                                    int32_t *nonfinite, uint32_t *partials, hipStream_t stream);
+hipError_t launch_quantize_mx(const void *x, gs_dtype dt, int64_t rows, int64_t cols, int fmt,
+                              uint8_t *codes, uint8_t *scales, int32_t *nonfinite,
+                              hipStream_t stream);
+hipError_t launch_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
+                                const uint8_t *scales, float *out, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
                              const float *scales, float *out, hipStream_t stream);
 

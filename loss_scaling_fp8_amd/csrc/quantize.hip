@@ -1,12 +1,16 @@
 // quantize.hip -- FP8 (OCP E4M3 / E5M2) scaled quantization at per-tensor,
-// 1x128 and 128x128 granularity, and the matching dequantization.
+// 1x128, 128x128 and 1x32 granularity (1x32 also with MX-style E8M0
+// scales), and the matching dequantization.
 //
 // What is computed ("Mixed precision and FP8 training", section "FP8
 // training", fp8_scaling.py: quant / per_tensor / per_block; "Why FP8
 // training is stable", Failure 1 and "The seam"): per block, the largest
 // finite |x| gives s = fl32(max(amax, 1e-12) / MAX); each element becomes
 // the FP8 code of clamp(fl32(x / s), -MAX, MAX) rounded to nearest-even; the
-// dequantized value is decode(code) * s in FP32.
+// dequantized value is decode(code) * s in FP32.  The 1x32 blocks are the
+// granularity of the MX formats (same page, hardware notes: one scaling
+// factor per 32 elements); their power-of-two E8M0 scale is the smallest
+// power of two not below the block scale above.
 //
 // Design (gfx950, wave64):
 //  * 1x128: a row-major matrix whose width is a multiple of 128 is a flat
@@ -14,6 +18,8 @@
 //    A lane owns 32 contiguous elements (4 x 16-byte loads of BF16), a quad
 //    of lanes owns a block: the block amax is two DPP quad exchanges, and
 //    each lane stores 32 codes (2 x 16 bytes).
+//  * 1x32 (and MX-style 1x32 with E8M0 power-of-two scales): the 1x128
+//    walk with one lane per block, so the amax needs no lane exchange.
 //  * 128x128: one 256-lane workgroup per tile, the whole tile held in
 //    registers (64 elements per lane); amax by DPP inside rows of 16 lanes,
 //    two cross-row shuffles, and 4 LDS words across the waves.
@@ -217,36 +223,52 @@ __device__ __forceinline__ void store_words(uint8_t *p, const uint32_t *w, int n
     for (; i < nwords; ++i) st<NT>(p + 4 * i, w[i]);
 }
 
-// ---------------------------------------------------------------- 1x128
-// Lanes per block: 4; each lane 32 elements (BF16: 4 vectors, FP32: 8).
-template <int FMT, int MODE, typename IN>
+// ---------------------------------------------------------------- 1x128, 1x32
+// A lane owns 32 contiguous elements (BF16: 4 vectors, FP32: 8), so a
+// 1x128 block is a quad of lanes (amax by DPP quad exchanges) and a 1x32
+// block is one lane; either way lane l of a wave reads bytes [64 l, 64 l +
+// 64) of the wave's span (BF16), the same access pattern.
+// MODE: FP8_SCALE_FROM_AMAX and FP8_SCALE_GIVEN (FP32 scales), or kModeMx:
+// the amax scale rounded up to a power of two, written as its E8M0 byte
+// (the FP32 exponent field: both biases are 127).
+constexpr int kModeMx = 2;
+
+template <int FMT, int MODE, typename IN, int BLOCK>
 __global__ __launch_bounds__(256)
-void quant_1x128_kernel(const IN *__restrict__ x, int64_t nblocks, uint8_t *__restrict__ codes,
-                        float *__restrict__ scales, int32_t *__restrict__ nonfinite) {
-    constexpr int kLanesPerBlock = 4;
-    constexpr int kElems = 128 / kLanesPerBlock;             // 32
+void quant_row_blocks_kernel(const IN *__restrict__ x, int64_t nblocks,
+                             uint8_t *__restrict__ codes, void *__restrict__ scales,
+                             int32_t *__restrict__ nonfinite) {
+    constexpr int kElems = 32;
+    constexpr int kLanesPerBlock = BLOCK / kElems;           // 4 or 1
     constexpr int NV = kElems * int(sizeof(IN)) / 16;
-    constexpr int kBlocksPerWG = 256 / kLanesPerBlock;       // 64
+    constexpr int kBlocksPerWG = 256 / kLanesPerBlock;
     const int sub = threadIdx.x & (kLanesPerBlock - 1);
     bool saw_nf = false;
     for (int64_t b = int64_t(blockIdx.x) * kBlocksPerWG + (threadIdx.x / kLanesPerBlock);
          b < nblocks; b += int64_t(gridDim.x) * kBlocksPerWG) {
         LaneData<IN, NV> L;
-        L.template load<GS_Q1_NT_LOAD>(x + b * 128 + sub * kElems);
+        L.template load<GS_Q1_NT_LOAD>(x + b * BLOCK + sub * kElems);
         uint32_t amax_bits;
         const bool nf = L.absmax(amax_bits);
         saw_nf |= nf;
         float s;
-        if (MODE == FP8_SCALE_FROM_AMAX) {
+        if (MODE == FP8_SCALE_GIVEN) {
+            s = static_cast<const float *>(scales)[b];
+        } else {
             amax_bits = group_max<kLanesPerBlock>(amax_bits);
             s = scale_from_amax<FMT>(as_f32(amax_bits));
-            if (sub == 0) scales[b] = s;
-        } else {
-            s = scales[b];
+            if (MODE == kModeMx) {
+                uint32_t sb = as_u32(s);                      // positive, normal, < 2^120
+                if (sb & 0x7FFFFFu) sb = (sb & 0x7F800000u) + 0x00800000u;
+                s = as_f32(sb);
+                if (sub == 0) static_cast<uint8_t *>(scales)[b] = (uint8_t)(sb >> 23);
+            } else if (sub == 0) {
+                static_cast<float *>(scales)[b] = s;
+            }
         }
         uint32_t out[kElems / 4];
         L.template cast<FMT, MODE == FP8_SCALE_GIVEN>(s, nf, out);
-        store_words<GS_Q1_NT_STORE>(codes + b * 128 + sub * kElems, out, kElems / 4);
+        store_words<GS_Q1_NT_STORE>(codes + b * BLOCK + sub * kElems, out, kElems / 4);
     }
     if (saw_nf && nonfinite) *nonfinite = 1;
 }
@@ -505,13 +527,22 @@ __device__ __forceinline__ float dequant_one(uint8_t c, float s) {
     return canon(v[0] * s);
 }
 
-// per-tensor (BLOCKED = false) or 1x128 (BLOCKED = true): flat walk over
-// groups of 4 codes; a 128-code block is 32 consecutive groups.
-template <int FMT, bool BLOCKED>
+// Scale of a 1x32 block from its E8M0 byte: 2^(b - 127), NaN for 0xFF
+// (b = 0 is the FP32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_scale(uint32_t b) {
+    return b == 0xFFu ? as_f32(0x7FC00000u) : as_f32(b ? (b << 23) : 0x00400000u);
+}
+
+// Flat walk over groups of 4 codes.  KIND: 0 per-tensor, 1 1x128 (a block is
+// 32 consecutive groups), 2 1x32 with FP32 scales (8 groups), 3 1x32 with
+// E8M0 scale bytes.
+template <int FMT, int KIND>
 __global__ __launch_bounds__(256)
 void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
-                           const float *__restrict__ scales, float *__restrict__ out) {
+                           const void *__restrict__ scales_v, float *__restrict__ out) {
     constexpr int U = 4;
+    constexpr bool BLOCKED = KIND != 0;
+    const float *scales = static_cast<const float *>(scales_v);
     const int64_t ngroups = n / 4;
     const float s0 = BLOCKED ? 0.0f : scales[0];
     const uint32_t *cw = reinterpret_cast<const uint32_t *>(codes);
@@ -527,7 +558,13 @@ void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + u * 256 + threadIdx.x;
-            if (g < ngroups) dequant_group<FMT>(w[u], BLOCKED ? scales[g >> 5] : s0, o4 + g);
+            if (g < ngroups) {
+                float s = s0;
+                if (KIND == 1) s = scales[g >> 5];
+                if (KIND == 2) s = scales[g >> 3];
+                if (KIND == 3) s = e8m0_scale(static_cast<const uint8_t *>(scales_v)[g >> 3]);
+                dequant_group<FMT>(w[u], s, o4 + g);
+            }
         }
     }
     if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - ngroups * 4) {
@@ -569,18 +606,26 @@ inline uint32_t grid_for(int64_t work_items, int64_t per_wg) {
     return (uint32_t)g;
 }
 
+template <int FMT, int MODE, typename IN, int BLOCK>
+hipError_t quantize_rows(const IN *x, int64_t n, uint8_t *codes, void *scales,
+                         int32_t *nonfinite, hipStream_t stream) {
+    const int64_t nblocks = n / BLOCK;
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((quant_row_blocks_kernel<FMT, MODE, IN, BLOCK>),
+                       dim3(grid_for(nblocks, 256 / (BLOCK / 32))), dim3(256), 0, stream, x,
+                       nblocks, codes, scales, nonfinite);
+    return hipGetLastError();
+}
+
 template <int FMT, int MODE, typename IN>
 hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uint8_t *codes,
                           float *scales, int32_t *nonfinite, uint32_t *partials,
                           hipStream_t stream) {
     const int64_t n = rows * cols;
-    if (gran == FP8_BLOCK_1x128) {
-        const int64_t nblocks = n / 128;
-        if (nblocks == 0) return hipSuccess;
-        hipLaunchKernelGGL((quant_1x128_kernel<FMT, MODE, IN>), dim3(grid_for(nblocks, 64)),
-                           dim3(256), 0, stream, x, nblocks, codes, scales, nonfinite);
-        return hipGetLastError();
-    }
+    if (gran == FP8_BLOCK_1x128)
+        return quantize_rows<FMT, MODE, IN, 128>(x, n, codes, scales, nonfinite, stream);
+    if (gran == FP8_BLOCK_1x32)
+        return quantize_rows<FMT, MODE, IN, 32>(x, n, codes, scales, nonfinite, stream);
     if (gran == FP8_BLOCK_128x128) {
         const int64_t tpr = cols / 128, ntiles = (rows / 128) * tpr;
         if (ntiles == 0) return hipSuccess;
@@ -640,12 +685,25 @@ hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int 
         return hipGetLastError();
     }
     if (n == 0) return hipSuccess;
+    const dim3 grid(grid_for(n / 4, 256 * 4));
     if (gran == FP8_BLOCK_1x128)
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, true>), dim3(grid_for(n / 4, 256 * 4)),
-                           dim3(256), 0, stream, codes, n, scales, out);
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 1>), grid, dim3(256), 0, stream, codes, n,
+                           scales, out);
+    else if (gran == FP8_BLOCK_1x32)
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 2>), grid, dim3(256), 0, stream, codes, n,
+                           scales, out);
     else
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, false>), dim3(grid_for(n / 4, 256 * 4)),
-                           dim3(256), 0, stream, codes, n, scales, out);
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 0>), grid, dim3(256), 0, stream, codes, n,
+                           scales, out);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t dequantize_mx_fmt(const uint8_t *codes, int64_t n, const uint8_t *scales, float *out,
+                             hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((dequant_linear_kernel<FMT, 3>), dim3(grid_for(n / 4, 256 * 4)), dim3(256),
+                       0, stream, codes, n, scales, out);
     return hipGetLastError();
 }
 
@@ -682,6 +740,30 @@ hipError_t launch_quantize_delayed(const void *x, gs_dtype dt, int64_t rows, int
         if (dt == GS_BF16) GS_QD(1, uint16_t); else GS_QD(1, float);
     }
 #undef GS_QD
+}
+
+hipError_t launch_quantize_mx(const void *x, gs_dtype dt, int64_t rows, int64_t cols, int fmt,
+                              uint8_t *codes, uint8_t *scales, int32_t *nonfinite,
+                              hipStream_t stream) {
+    const int64_t n = rows * cols;
+    if (fmt == FP8_E4M3) {
+        if (dt == GS_BF16)
+            return quantize_rows<0, kModeMx, uint16_t, 32>(static_cast<const uint16_t *>(x), n,
+                                                           codes, scales, nonfinite, stream);
+        return quantize_rows<0, kModeMx, float, 32>(static_cast<const float *>(x), n, codes,
+                                                    scales, nonfinite, stream);
+    }
+    if (dt == GS_BF16)
+        return quantize_rows<1, kModeMx, uint16_t, 32>(static_cast<const uint16_t *>(x), n, codes,
+                                                       scales, nonfinite, stream);
+    return quantize_rows<1, kModeMx, float, 32>(static_cast<const float *>(x), n, codes, scales,
+                                                nonfinite, stream);
+}
+
+hipError_t launch_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
+                                const uint8_t *scales, float *out, hipStream_t stream) {
+    if (fmt == FP8_E4M3) return dequantize_mx_fmt<0>(codes, rows * cols, scales, out, stream);
+    return dequantize_mx_fmt<1>(codes, rows * cols, scales, out, stream);
 }
 
 hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,

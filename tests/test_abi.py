@@ -86,7 +86,7 @@ def test_update_argument_errors():
 @pytest.mark.parametrize("args,code", [
     ((FAKE, 1, 128, 128, 0, 1, 0), -4),        # FP16 input not supported
     ((FAKE, 2, 128, 128, 2, 1, 0), -5),        # bad format
-    ((FAKE, 2, 128, 128, 0, 3, 0), -5),        # bad granularity
+    ((FAKE, 2, 128, 128, 0, 4, 0), -5),        # bad granularity
     ((FAKE, 2, 128, 128, 0, 1, 2), -5),        # bad mode
     ((FAKE, 2, 128, 100, 0, 1, 0), -3),        # 1x128 needs cols % 128
     ((FAKE, 2, 100, 128, 0, 2, 0), -3),        # 128x128 needs rows % 128
@@ -197,3 +197,23 @@ def test_update_hysteresis_argument_errors():
     assert call(m=float("nan")) == -5
     assert call(g=float("inf")) == -5
     assert call(b=0.0) == -5
+
+
+def test_mx_and_1x32_argument_errors():
+    L = gs.lib()
+    q, d = L.fp8_quantize_mx, L.fp8_dequantize_mx
+    assert q(FAKE, 1, 4, 64, 0, FAKE, FAKE, None, None) == -4          # FP16 input
+    assert q(FAKE, 2, 4, 64, 2, FAKE, FAKE, None, None) == -5          # bad format
+    assert q(FAKE, 2, 4, 48, 0, FAKE, FAKE, None, None) == -3          # cols % 32
+    assert q(FAKE, 2, -1, 64, 0, FAKE, FAKE, None, None) == -2
+    assert q(None, 2, 4, 64, 0, FAKE, FAKE, None, None) == -1
+    assert q(FAKE, 2, 4, 64, 0, FAKE, None, None, None) == -1
+    assert q(FAKE + 8, 2, 4, 64, 0, FAKE, FAKE, None, None) == -6
+    assert q(None, 2, 0, 64, 0, None, None, None, None) == 0          # empty
+    assert d(FAKE, 4, 48, 0, FAKE, FAKE, None) == -3
+    assert d(FAKE, 4, 64, 0, None, FAKE, None) == -1
+    assert d(FAKE, 4, 64, 0, FAKE, FAKE + 4, None) == -6
+    assert d(None, 0, 64, 0, None, None, None) == 0
+    assert L.fp8_quantize(FAKE, 2, 4, 48, 0, 3, 0, FAKE, FAKE, None, None, 0, None) == -3
+    assert L.fp8_dequantize(FAKE, 4, 48, 0, 3, FAKE, FAKE, None) == -3
+    assert L.fp8_quantize(FAKE, 2, 4, 64, 0, 4, 0, FAKE, FAKE, None, None, 0, None) == -5

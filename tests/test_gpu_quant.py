@@ -11,7 +11,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 E4M3, E5M2 = gs.FP8_E4M3, gs.FP8_E5M2
-PT, B1, B128 = gs.FP8_PER_TENSOR, gs.FP8_BLOCK_1x128, gs.FP8_BLOCK_128x128
+PT, B1, B128, B32 = gs.FP8_PER_TENSOR, gs.FP8_BLOCK_1x128, gs.FP8_BLOCK_128x128, gs.FP8_BLOCK_1x32
 
 
 @pytest.fixture(scope="module")
@@ -85,10 +85,11 @@ def _check(x_host, fmt, gran, mode, dev, scales_host=None):
 
 SHAPES = {PT: [(1, 1), (3, 5), (7, 129), (1000, 999), (1024, 1024)],
           B1: [(1, 128), (3, 384), (130, 256), (257, 640)],
-          B128: [(128, 128), (256, 384), (384, 640)]}
+          B128: [(128, 128), (256, 384), (384, 640)],
+          B32: [(1, 32), (3, 96), (130, 256), (257, 608)]}
 
 
-@pytest.mark.parametrize("gran", [PT, B1, B128])
+@pytest.mark.parametrize("gran", [PT, B1, B128, B32])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quantize_special_values_all_shapes(gran, fmt, dtype, dev):
@@ -99,7 +100,7 @@ def test_quantize_special_values_all_shapes(gran, fmt, dtype, dev):
         _check(np.ascontiguousarray(x), fmt, gran, gs.FP8_SCALE_FROM_AMAX, dev)
 
 
-@pytest.mark.parametrize("gran", [PT, B1, B128])
+@pytest.mark.parametrize("gran", [PT, B1, B128, B32])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_quantize_given_scales_including_degenerate(gran, fmt, dev):
     rng = np.random.default_rng(77 + gran + 3 * fmt)
@@ -151,7 +152,8 @@ def test_every_bf16_x_amax_pair(fmt, dev):
 def test_dequantize_all_codes_all_granularities(dev):
     rng = np.random.default_rng(5)
     for fmt in (E4M3, E5M2):
-        for gran, (rows, cols) in ((PT, (16, 16)), (B1, (2, 256)), (B128, (128, 256))):
+        for gran, (rows, cols) in ((PT, (16, 16)), (B1, (2, 256)), (B128, (128, 256)),
+                                   (B32, (2, 256))):
             codes = np.tile(np.arange(256, dtype=np.uint8), rows * cols // 256).reshape(rows, cols)
             ns = oracle.n_scales(rows, cols, gran)
             for sc in (np.float32([1.0] * ns), rng.uniform(1e-3, 10, ns).astype(np.float32),
