@@ -89,11 +89,15 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
 
 
 def _time_launches(fn, reps, flush=None):
-    """Median and minimum milliseconds of fn() over reps runs, HIP events on
-    the current stream; flush() (not timed) runs before each."""
+    """Median and minimum milliseconds of fn() over reps launches, from HIP
+    events recorded on the current stream around each launch; flush() (not
+    timed) is enqueued before each.  Everything is enqueued before the one
+    wait at the end, so the GPU is busy with earlier work while the host
+    marshals each call and the events time the GPU work only (the first
+    launch may include host latency; the median ignores it)."""
     import numpy as np
     import torch
-    ts = []
+    evs = []
     for _ in range(reps):
         if flush is not None:
             flush()
@@ -101,8 +105,9 @@ def _time_launches(fn, reps, flush=None):
         a.record()
         fn()
         b.record()
-        b.synchronize()
-        ts.append(a.elapsed_time(b))
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
     return float(np.median(ts)), float(np.min(ts))
 
 
@@ -390,19 +395,17 @@ def main():
 
     # 1x32 blocks (FP32 scales, and MX-style E8M0 scales) on the activation
     # shape, outside the timed step, with the 1x128 pair timed the same way
-    # for reference.  Before each timed launch a 1 GiB write and a 1 GiB read
-    # (synchronised) leave the infinity cache holding clean lines of other
-    # buffers: cold inputs, and no write-back of an unrelated kernel's dirty
-    # lines charged to the launch.
+    # for reference.  Before each timed launch a 1 GiB write and then a 1 GiB
+    # read (stream-ordered) leave the infinity cache holding clean lines of
+    # other buffers: cold inputs, and no write-back of an unrelated kernel's
+    # dirty lines charged to the launch.
     if not args.pmc_safe:
         junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
         def flush():
             junk.fill_(1.0)
-            torch.cuda.synchronize()
             junk_rd.sum()
-            torch.cuda.synchronize()
         s32 = torch.empty(gs.scale_shape(act.rows, act.cols, gs.FP8_BLOCK_1x32),
                           dtype=torch.float32, device=dev)
         smx = torch.empty((act.rows, act.cols // 32), dtype=torch.uint8, device=dev)
