@@ -214,8 +214,9 @@ def main():
                          "configurations (reported under \"configs\")")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 6 plain copy kernels of 1 GiB (for HBM counter calibration)")
-    ap.add_argument("--sumsq", action="store_true",
-                    help="with --pmc-safe: also run the unscale + sum-of-squares variant")
+    ap.add_argument("--extensions", "--sumsq", dest="extensions", action="store_true",
+                    help="with --pmc-safe: also run the launches outside the step (unscale + "
+                         "sum of squares, 1x32 and MX blocks)")
     ap.add_argument("--pmc-safe", action="store_true",
                     help="for rocprofv3 --pmc runs: constant inputs (few kernel launches), no "
                          "device-to-device or device-to-host memcpy, no copy ceiling, no "
@@ -373,7 +374,7 @@ def main():
     # unscale fused with the exact gradient sum of squares, on the same
     # resident gradient set (outside the timed step; own HIP events)
     ext = {}
-    if not args.pmc_safe or args.sumsq:
+    if not args.pmc_safe or args.extensions:
         acc = torch.zeros(2, dtype=torch.int64, device=dev)
         nsq = torch.empty(1, dtype=torch.float64, device=dev)
         ws = torch.empty(gs.gs_unscale_check_sumsq_workspace_size([g.numel() for g in grads]),
@@ -399,7 +400,7 @@ def main():
     # read (stream-ordered) leave the infinity cache holding clean lines of
     # other buffers: cold inputs, and no write-back of an unrelated kernel's
     # dirty lines charged to the launch.
-    if not args.pmc_safe:
+    if not args.pmc_safe or args.extensions:
         junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
@@ -423,7 +424,7 @@ def main():
                 ("dequant_mx_e8m0", lambda: gs.fp8_dequantize_mx(ca, act.fmt, smx, da),
                  n_a * 5 + nb32)):
             fn()
-            ms_k, _ = _time_launches(fn, 20, flush)
+            ms_k, _ = _time_launches(fn, 20, None if args.pmc_safe else flush)
             gbps = nbytes / (ms_k * 1e-3) / 1e9
             ext[name] = {"ms": round(ms_k, 4), "bytes": nbytes, "GBps": round(gbps, 1),
                          "frac_of_peak": round(gbps / PEAK_GBPS, 4),
