@@ -58,6 +58,9 @@
 #ifndef GS_QT_NT_STORE
 #define GS_QT_NT_STORE 0
 #endif
+#ifndef Q128_THREADS
+#define Q128_THREADS 256
+#endif
 
 namespace gsk {
 
@@ -171,12 +174,19 @@ struct LaneData {
     // a NaN or an Inf then rewrites just those codes: NaN -> sign|0x7F,
     // +-Inf -> +-MAX (Inf / s is infinite for a finite positive s, and the
     // clamp saturates it).  Other scales (0, negative, non-finite, tiny or
-    // huge: only possible when given) take the IEEE division per element.
-    template <int FMT, bool CLAMP>
+    // huge) take the IEEE division per element; they can only be given, so
+    // that path is compiled only when GIVEN (a scale from a block amax is
+    // always in the fast range, and leaving the path out frees registers).
+    // The fix-up runs per group of 4 right after that group's codes, so its
+    // inputs are live anyway: done as one pass after the whole lane, it kept
+    // every unpacked element alive and cost 34 VGPRs (128x128: 130 -> 68
+    // together with the fast-only amax path, 3 -> 7 workgroups per CU).
+    template <int FMT, bool GIVEN>
     __device__ __forceinline__ void cast(float s, bool lane_nonfinite,
                                          uint32_t (&out)[kElems / 4]) const {
         const float r = 1.0f / s;
-        if (fast_scale(s)) {
+        if (!GIVEN || fast_scale(s)) {
+            constexpr uint32_t kMaxCode = FMT == 0 ? 0x7Eu : 0x7Bu;
 #pragma unroll
             for (int j = 0; j < kElems / 4; ++j) {
                 float q[4];
@@ -184,22 +194,21 @@ struct LaneData {
                 for (int k = 0; k < 4; ++k) {
                     const uint32_t e = elem(4 * j + k);
                     float a = div_by_scale(__builtin_fabsf(as_f32(e)), s, r);
-                    if (CLAMP) a = as_f32(min(as_u32(a), Fp8<FMT>::kMaxBits));
+                    if (GIVEN) a = as_f32(min(as_u32(a), Fp8<FMT>::kMaxBits));
                     q[k] = as_f32(as_u32(a) | (e & 0x80000000u));
                 }
-                out[j] = cvt_pk<FMT, true>(q[2], q[3], cvt_pk<FMT, false>(q[0], q[1], 0u));
-            }
-            if (lane_nonfinite) {
-                constexpr uint32_t kMaxCode = FMT == 0 ? 0x7Eu : 0x7Bu;
+                uint32_t o = cvt_pk<FMT, true>(q[2], q[3], cvt_pk<FMT, false>(q[0], q[1], 0u));
+                if (lane_nonfinite) {
 #pragma unroll
-                for (int i = 0; i < kElems; ++i) {
-                    const uint32_t e = elem(i);
-                    if ((e & 0x7F800000u) == 0x7F800000u) {
-                        const uint32_t c = ((e >> 24) & 0x80u) | ((e & 0x7FFFFFu) ? 0x7Fu : kMaxCode);
-                        const int sh = 8 * (i & 3);
-                        out[i >> 2] = (out[i >> 2] & ~(0xFFu << sh)) | (c << sh);
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t e = elem(4 * j + k);
+                        if ((e & 0x7F800000u) == 0x7F800000u) {
+                            const uint32_t c = ((e >> 24) & 0x80u) | ((e & 0x7FFFFFu) ? 0x7Fu : kMaxCode);
+                            o = (o & ~(0xFFu << (8 * k))) | (c << (8 * k));
+                        }
                     }
                 }
+                out[j] = o;
             }
         } else {
 #pragma unroll
@@ -274,18 +283,20 @@ void quant_row_blocks_kernel(const IN *__restrict__ x, int64_t nblocks,
 }
 
 // ---------------------------------------------------------------- 128x128
-// One workgroup per tile.  Threads per 128-element row: 16 (BF16) or 32
-// (FP32), one 16-byte vector each; the tile takes 8 or 16 row passes.
-template <int FMT, int MODE, typename IN>
-__global__ __launch_bounds__(256)
+// One workgroup of T lanes per tile.  Threads per 128-element row: 16 (BF16)
+// or 32 (FP32), one 16-byte vector each; the tile takes 128 / (T / threads
+// per row) row passes.
+template <int FMT, int MODE, typename IN, int T = Q128_THREADS>
+__global__ __launch_bounds__(T)
 void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_per_row,
                           int64_t ntiles, uint8_t *__restrict__ codes, float *__restrict__ scales,
                           int32_t *__restrict__ nonfinite) {
     constexpr int kPerVec = 16 / int(sizeof(IN));
     constexpr int kThreadsPerRow = 128 / kPerVec;
-    constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+    constexpr int kRowsPerPass = T / kThreadsPerRow;
     constexpr int kPasses = 128 / kRowsPerPass;
-    __shared__ uint32_t red[4];
+    constexpr int kWaves = T / 64;
+    __shared__ uint32_t red[kWaves];
     const int tid = threadIdx.x;
     const int row0 = tid / kThreadsPerRow;
     const int seg = tid % kThreadsPerRow;
@@ -303,7 +314,9 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
             amax_bits = wave_max(amax_bits);
             if ((tid & 63) == 0) red[tid >> 6] = amax_bits;
             __syncthreads();
-            amax_bits = max(max(red[0], red[1]), max(red[2], red[3]));
+            amax_bits = red[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) amax_bits = max(amax_bits, red[w]);
             __syncthreads();                  // red[] is reused by the next tile
             s = scale_from_amax<FMT>(as_f32(amax_bits));
             if (tid == 0) scales[t] = s;
@@ -405,7 +418,7 @@ void amax_finalize_kernel(const uint32_t *__restrict__ partials, int nparts,
 // With EMIT (delayed scaling), each workgroup also writes the largest finite
 // |x| it saw to partials[blockIdx.x]; the grid then has <= kPartialSlots
 // workgroups.
-template <int FMT, bool CLAMP, typename IN, bool EMIT = false>
+template <int FMT, bool GIVEN, typename IN, bool EMIT = false>
 __global__ __launch_bounds__(256)
 void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, uint8_t *__restrict__ codes,
                          const float *__restrict__ scales, int32_t *__restrict__ nonfinite,
@@ -432,7 +445,7 @@ void quant_tensor_kernel(const IN *__restrict__ x, int64_t n, uint8_t *__restric
                 saw_nf |= nf;
                 m = max(m, a);
                 uint32_t out[kPerVec / 4];
-                L[u].template cast<FMT, CLAMP>(s, nf, out);
+                L[u].template cast<FMT, GIVEN>(s, nf, out);
                 store_words<GS_QT_NT_STORE>(codes + v * kPerVec, out, kPerVec / 4);
             }
         }
@@ -630,7 +643,8 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
         const int64_t tpr = cols / 128, ntiles = (rows / 128) * tpr;
         if (ntiles == 0) return hipSuccess;
         hipLaunchKernelGGL((quant_128x128_kernel<FMT, MODE, IN>), dim3(grid_for(ntiles, 1)),
-                           dim3(256), 0, stream, x, cols, tpr, ntiles, codes, scales, nonfinite);
+                           dim3(Q128_THREADS), 0, stream, x, cols, tpr, ntiles, codes, scales,
+                           nonfinite);
         return hipGetLastError();
     }
     // per-tensor: partial maxima, the scale, the cast (given mode: the cast)
