@@ -223,3 +223,58 @@ def test_special_values_4gib_all_modes(dev):
         torch.cuda.empty_cache()
     print("special values: %d blocks and %d sampled elements checked" % (blocks_checked, elems_checked))
     assert blocks_checked >= 4 * 2 * (380 + 6) and elems_checked >= 4 * 2 * 4 * 190000
+
+
+def _check_row32_blocks(x_spec, codes, scales, deq, mx, fmt, rng, nsample):
+    """Sampled 1x32 blocks (FP32 scales, or MX E8M0 bytes when mx) against
+    the oracle on the block regenerated on the host."""
+    rows, cols = x_spec.rows, x_spec.cols
+    nb = rows * (cols // 32)
+    blocks = np.unique(np.concatenate([rng.integers(0, nb, nsample), [0, nb - 1]]))
+    for b in blocks:
+        r, j = divmod(int(b), cols // 32)
+        idx = torch.arange(r * cols + j * 32, r * cols + j * 32 + 32)
+        xb = x_spec.gen(idx).numpy().astype(np.uint16).reshape(1, 32)
+        sl = (slice(r, r + 1), slice(j * 32, (j + 1) * 32))
+        if mx:
+            rc, rs, _ = oracle.quantize_mx(xb, fmt)
+            rd = oracle.dequantize_mx(rc, fmt, rs)
+            assert int(scales[r, j].item()) == int(rs[0, 0]), b
+        else:
+            rc, rs, _ = oracle.quantize(xb, fmt, PT)
+            rd = oracle.dequantize(rc, fmt, PT, rs)
+            assert _u32(scales[r, j:j + 1])[0] == rs.view(np.uint32)[0], b
+        assert np.array_equal(codes[sl].cpu().numpy(), rc), b
+        assert np.array_equal(_u32(deq[sl]).reshape(-1), rd.reshape(-1).view(np.uint32)), b
+    return len(blocks)
+
+
+def test_row32_and_mx_blocks_at_full_size(dev):
+    """1x32 (FP32 scales) and MX 1x32 (E8M0) on the DeepSeek-V3 activation
+    shape and on the four 16384x32768 special-value tensors: sampled blocks
+    against the oracle, and the nonfinite flag over the whole tensor."""
+    rng = np.random.default_rng(66)
+    act = synth.deepseek_v3_blocks()[0]
+    checked = 0
+    for sp, fmts, nsample in [(act, (gs.FP8_E4M3,), 3000)] + \
+            [(s, (gs.FP8_E4M3, gs.FP8_E5M2), 400) for s in synth.special_values_4gib()]:
+        x = sp.full(dev)
+        expect_nf = None
+        for fmt in fmts:
+            for mx in (False, True):
+                nf = torch.zeros(1, dtype=torch.int32, device=dev)
+                if mx:
+                    codes, scales = gs.fp8_quantize_mx(x, fmt, nonfinite=nf)
+                    deq = gs.fp8_dequantize_mx(codes, fmt, scales)
+                else:
+                    codes, scales = gs.fp8_quantize(x, fmt, gs.FP8_BLOCK_1x32, nonfinite=nf)
+                    deq = gs.fp8_dequantize(codes, fmt, gs.FP8_BLOCK_1x32, scales)
+                torch.cuda.synchronize()
+                if expect_nf is None:
+                    expect_nf = int((~torch.isfinite(x.float())).any().item())
+                assert int(nf.item()) == expect_nf, (sp.name, fmt, mx)
+                checked += _check_row32_blocks(sp, codes, scales, deq, mx, fmt, rng, nsample)
+                del codes, scales, deq
+        del x
+        torch.cuda.empty_cache()
+    assert checked >= 2 * 2900 + 4 * 2 * 2 * 380
