@@ -8,7 +8,11 @@
  * hipStream_t; NULL means the null stream), asynchronously: no call
  * synchronises the host, reads device memory from the host, or allocates on
  * a repeated call with the same arguments.  Device buffers must stay alive
- * until the enqueued work has finished.
+ * until the enqueued work has finished.  The one exception is the first
+ * call of gs_unscale_check / gs_unscale_check_sumsq with a new gradient
+ * list: it allocates the list's chunk descriptors and uploads them with a
+ * blocking copy (and evicting an old list from the cache waits for the
+ * device); repeated calls with the same list do neither.
  *
  * Errors: argument errors are detected on the host and returned before
  * anything is enqueued, with no side effects.  Non-finite DATA is never an
@@ -87,7 +91,8 @@ typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
  * sizes) are built on the first call with a given (grads, outs, numels) list
  * and cached on the device (at most 64 lists / 1 GiB, least recently used
  * evicted; an eviction waits for the device), so a repeated call with the
- * same list uploads nothing.  Device addresses must lie below 2^48
+ * same list uploads nothing.  That first call allocates and uploads
+ * synchronously (the upload has finished when the call returns).  Device addresses must lie below 2^48
  * (GS_ERR_ARG otherwise; every current AMD GPU address does).
  */
 gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *outs,
