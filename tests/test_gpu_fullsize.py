@@ -278,3 +278,64 @@ def test_row32_and_mx_blocks_at_full_size(dev):
         del x
         torch.cuda.empty_cache()
     assert checked >= 2 * 2900 + 4 * 2 * 2 * 380
+
+
+def test_tensors_above_2_32_elements(dev):
+    """Maximum sizes: one FP16 gradient tensor of 2^32 + 6149 elements and
+    one 32896x131072 BF16 matrix (4.31e9 elements; the 1x128 and dequantize
+    grids are capped and stride).  Sampled outputs around the 2^31 and 2^32
+    element boundaries and at both ends against the oracle; an Inf past
+    2^32 sets the flag; the exact sum of squares against an FP64 sum."""
+    n = (1 << 32) + 3 * 2048 + 5
+    g = synth.GradSet(seed=7007, scale=2.0 ** 15, log2_lo=-18.0, log2_hi=12.0, steps=1)
+    g.tensors = [synth.GradSpec("big", n, 1)]
+    grad = g.full(0, dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    S = torch.tensor([g.scale], dtype=torch.float32, device=dev)
+    f = torch.zeros(1, dtype=torch.int32, device=dev)
+    acc = torch.zeros(2, dtype=torch.int64, device=dev)
+    nsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    gs.gs_unscale_check_sumsq([grad], [out], S, f, acc, nsq)
+    torch.cuda.synchronize()
+    assert int(f.item()) == 0
+    rng = np.random.default_rng(77)
+    edges = [np.arange(0, 4096), np.arange(n - 4096, n),
+             np.arange((1 << 31) - 2048, (1 << 31) + 2048), np.arange((1 << 32) - 2048, (1 << 32) + 2048)]
+    idx = np.unique(np.concatenate(edges + [rng.integers(0, n, 50000)]))
+    ti = torch.from_numpy(idx)
+    bits = g.gen(0, ti).numpy().astype(np.uint16)
+    ref, _ = oracle.unscale_check([bits], g.scale)
+    assert np.array_equal(_u32(out[ti.to(dev)]), ref[0].view(np.uint32))
+    tot = 0.0
+    for lo in range(0, n, 1 << 28):
+        tot += float((out[lo:lo + (1 << 28)].double() ** 2).sum().item())
+    assert abs(float(nsq.item()) - tot) <= 1e-12 * tot
+    pos = (1 << 32) + 7
+    grad[pos:pos + 1].fill_(float("inf"))
+    gs.gs_unscale_check([grad], [out], S, f)
+    torch.cuda.synchronize()
+    assert int(f.item()) == 1 and out[pos].item() == float("inf")
+    del grad, out
+    torch.cuda.empty_cache()
+
+    sp = synth.BitsSpec("big_random", 32896, 131072, 7007, 2, "random")
+    x = sp.full(dev)
+    for gran in (B1, B128):
+        codes, scales = gs.fp8_quantize(x, gs.FP8_E4M3, gran)
+        deq = gs.fp8_dequantize(codes, gs.FP8_E4M3, gran, scales)
+        torch.cuda.synchronize()
+        nb = _check_blocks(sp, codes, scales, deq, gran, gs.FP8_E4M3, rng, 600 if gran == B1 else 20)
+        assert nb >= (500 if gran == B1 else 15)
+        # the first and last block of the row that starts at element 2^32
+        if gran == B1:
+            r = (1 << 32) // sp.cols
+            for j in (0, sp.cols // 128 - 1):
+                idx = torch.arange(r * sp.cols + j * 128, r * sp.cols + j * 128 + 128)
+                xb = sp.gen(idx).numpy().astype(np.uint16).reshape(1, 128)
+                rc, rs, _ = oracle.quantize(xb, gs.FP8_E4M3, PT)
+                assert np.array_equal(codes[r, j * 128:(j + 1) * 128].cpu().numpy(), rc.reshape(-1))
+        del codes, scales, deq
+    codes, sc = gs.fp8_quantize_mx(x, gs.FP8_E5M2)
+    deq = gs.fp8_dequantize_mx(codes, gs.FP8_E5M2, sc)
+    torch.cuda.synchronize()
+    assert _check_row32_blocks(sp, codes, sc, deq, True, gs.FP8_E5M2, rng, 600) >= 500
