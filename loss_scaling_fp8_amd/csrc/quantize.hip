@@ -23,14 +23,18 @@
 //  * 128x128: one 256-lane workgroup per tile, the whole tile held in
 //    registers (64 elements per lane); amax by DPP inside rows of 16 lanes,
 //    two cross-row shuffles, and 4 LDS words across the waves.
-//  * per-tensor: the scale depends on the whole tensor, so two launches: a
-//    persistent pass writes one partial max per workgroup (no atomics, no
-//    zero-initialised memory), then the cast pass reduces the <= 1024
-//    partials in every workgroup and streams the tensor again.
+//  * per-tensor: the scale depends on the whole tensor, so three launches:
+//    a pass writes one partial max per workgroup (<= 8192; no atomics, no
+//    zero-initialised memory), one 1024-lane workgroup turns them into the
+//    scale, and the cast pass streams the tensor again.  Both passes use the
+//    1x128 lane layout (a lane owns 32 contiguous elements).  Delayed
+//    scaling casts with the previous scale and emits the partials in the
+//    same pass, then updates the history in one workgroup.
 //  * Division: x / s is formed from r = fl32(1/s) and one FMA correction
 //    (div_by_scale) whenever s is in the range where that reproduces the
-//    IEEE quotient's FP8 code, else by IEEE division.  Lanes holding a NaN
-//    or Inf take the exact per-element path; amax ignores them.
+//    IEEE quotient's FP8 code, else by IEEE division (only a given scale
+//    can be outside that range).  Lanes holding a NaN or Inf keep the fast
+//    path and then rewrite just those codes; amax ignores them.
 //  * The max-abs is taken on bit patterns: for non-negative floats unsigned
 //    integer order is numeric order, and BF16 halves are maxed pairwise.
 #include "device_fp8.hpp"
@@ -48,9 +52,6 @@
 #endif
 #ifndef GS_Q128_NT_STORE
 #define GS_Q128_NT_STORE 0
-#endif
-#ifndef GS_QT1_NT_LOAD
-#define GS_QT1_NT_LOAD 1
 #endif
 #ifndef GS_QT_NT_LOAD
 #define GS_QT_NT_LOAD 0
@@ -340,38 +341,62 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
 }
 
 // ---------------------------------------------------------------- per-tensor
-// Pass 1: one partial finite max (FP32 bits) per workgroup.  A work unit is
-// 4 x 256 consecutive 16-byte vectors (each wave-wide load instruction reads
-// 1 KiB of contiguous input); workgroups take units in a grid-stride loop.
-template <typename IN>
+// Pass 1: one partial finite max (FP32 bits) per workgroup (<= 8192
+// workgroups, grid-stride).  Two layouts, chosen by the tensor's size:
+//  * the tensor fits in the 256 MB infinity cache (STREAM = false): the lane
+//    layout of the cast below, a lane reading a piece of 32 contiguous
+//    elements with plain loads, so the cast's second read hits the cache;
+//  * larger tensors (STREAM = true): units of 4 x 256 consecutive 16-byte
+//    vectors (each wave-wide load reads 1 KiB of contiguous input) with
+//    non-temporal loads.
+// Measured on MI355X: 8192x8192 BF16 61.4 -> 59.1 us with the first for the
+// whole quantize, four 16384x32768 BF16 tensors 3.70 -> 3.49 TB/s with it,
+// hence the switch.  Workgroup 0 takes the elements past the last whole
+// piece / vector.
+constexpr int64_t kCacheResidentBytes = int64_t(192) << 20;
+
+template <typename IN, bool STREAM>
 __global__ __launch_bounds__(256)
 void amax_partials_kernel(const IN *__restrict__ x, int64_t n, uint32_t *__restrict__ partials,
                           int32_t *__restrict__ nonfinite) {
-    constexpr int kPerVec = 16 / int(sizeof(IN));
-    constexpr int U = 4;
+    constexpr int kStep = STREAM ? 16 / int(sizeof(IN)) : 32;   // elements per lane load unit
     __shared__ uint32_t red[4];
-    const int64_t nvec = n / kPerVec;
+    const int64_t nunits = n / kStep;
     uint32_t m = 0;
     bool nf = false;
-    for (int64_t v0 = int64_t(blockIdx.x) * 256 * U; v0 < nvec; v0 += int64_t(gridDim.x) * 256 * U) {
-        LaneData<IN, 1> L[U];
+    if constexpr (STREAM) {
+        constexpr int U = 4;
+        for (int64_t v0 = int64_t(blockIdx.x) * 256 * U; v0 < nunits;
+             v0 += int64_t(gridDim.x) * 256 * U) {
+            LaneData<IN, 1> L[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t v = v0 + u * 256 + threadIdx.x;
-            if (v < nvec) L[u].template load<GS_QT1_NT_LOAD>(x + v * kPerVec);
-        }
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = v0 + u * 256 + threadIdx.x;
+                if (v < nunits) L[u].template load<true>(x + v * kStep);
+            }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t v = v0 + u * 256 + threadIdx.x;
-            if (v < nvec) {
-                uint32_t a;
-                nf |= L[u].absmax(a);
-                m = max(m, a);
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = v0 + u * 256 + threadIdx.x;
+                if (v < nunits) {
+                    uint32_t a;
+                    nf |= L[u].absmax(a);
+                    m = max(m, a);
+                }
             }
         }
+    } else {
+        constexpr int NV = kStep * int(sizeof(IN)) / 16;
+        for (int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x; b < nunits;
+             b += int64_t(gridDim.x) * 256) {
+            LaneData<IN, NV> L;
+            L.template load<false>(x + b * kStep);
+            uint32_t a;
+            nf |= L.absmax(a);
+            m = max(m, a);
+        }
     }
-    if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPerVec) {     // ragged tail
-        const IN *p = x + nvec * kPerVec + threadIdx.x;
+    if (blockIdx.x == 0 && threadIdx.x < n - nunits * kStep) {     // ragged tail
+        const IN *p = x + nunits * kStep + threadIdx.x;
         uint32_t b;
         if constexpr (sizeof(IN) == 2) b = uint32_t(*reinterpret_cast<const uint16_t *>(p)) << 16;
         else b = *reinterpret_cast<const uint32_t *>(p);
@@ -643,13 +668,18 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
         return hipGetLastError();
     }
     // per-tensor: partial maxima, the scale, the cast (given mode: the cast)
-    constexpr int kPerVec = 16 / int(sizeof(IN));
     if (MODE == FP8_SCALE_FROM_AMAX) {
-        int64_t p = (n / kPerVec + 256 * 4 - 1) / (256 * 4);       // >= 4 vectors per lane
+        const bool stream_big = n * int64_t(sizeof(IN)) > kCacheResidentBytes;
+        const int64_t unit = stream_big ? 16 / int64_t(sizeof(IN)) * 256 * 4 : 32 * 256;
+        int64_t p = (n + unit - 1) / unit;
         if (p < 1) p = 1;
         if (p > kPartialSlots) p = kPartialSlots;
-        hipLaunchKernelGGL((amax_partials_kernel<IN>), dim3((uint32_t)p), dim3(256), 0, stream, x,
-                           n, partials, nonfinite);
+        if (stream_big)
+            hipLaunchKernelGGL((amax_partials_kernel<IN, true>), dim3((uint32_t)p), dim3(256), 0,
+                               stream, x, n, partials, nonfinite);
+        else
+            hipLaunchKernelGGL((amax_partials_kernel<IN, false>), dim3((uint32_t)p), dim3(256), 0,
+                               stream, x, n, partials, nonfinite);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((amax_finalize_kernel<FMT>), dim3(1), dim3(1024), 0, stream, partials,
