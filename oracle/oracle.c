@@ -418,18 +418,18 @@ int orc_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
     return 0;
 }
 
-/* Delayed per-tensor scaling, [WHY] Failure 1 ("keep a short history of
- * recent max-abs values and derive s from that"; the scale applied this step
- * comes from earlier steps) and the [MP] "FP8 training" figure ("per tensor
- * (delayed, from recent amax)").  One step:
+/* Delayed per-tensor scaling, [WHY] Failure 1 (the scale comes from a short
+ * history of recent max-abs values, so the scale applied this step reflects
+ * earlier steps) and the [MP] "FP8 training" figure (per-tensor scaling
+ * taken from recent amax values).  One step:
  *   1. codes = quant(x, s) with s = *scale_state (the given-scale cast:
  *      divide, clamp, round to nearest even);
  *   2. amax_t = largest finite |x| (0 if none);
  *   3. history[p] = amax_t with p = *pos mod H; *pos = (p + 1) mod H;
  *   4. *scale_state = fl32(max(max over the H history entries, 1e-12) / MAX),
  *      the scale for the next step.
- * Reading: "derive s from that" is taken as the maximum over the window (the
- * scale then covers every recent amax).  *scale_used receives the s of
+ * Reading: the pages do not say how s follows from the history; it is taken
+ * as the maximum over the window (the scale then covers every recent amax).  *scale_used receives the s of
  * step 1 (the dequantisation multiplier of these codes). */
 int orc_quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
                          float *scale_state, float *history, int32_t hlen, int32_t *pos,

@@ -101,8 +101,8 @@ def test_growth_every_window_refills_the_budget():
 
 
 def test_growth_twice_as_eager_as_gradscaler():
-    """The page: the 1000-step window probes upward twice as eagerly as
-    GradScaler's 2000-step interval."""
+    """The page's comparison: with a window half GradScaler's 2000-step
+    interval, this policy tries a larger scale twice as often."""
     flags = [0] * 6000
     ds = _run(flags)
     pt = _run_pt(flags)
@@ -110,10 +110,11 @@ def test_growth_twice_as_eager_as_gradscaler():
 
 
 def test_skip_rate_differs_from_the_same_start():
-    """The page: porting a recipe between the two policies changes the skip
-    rate even with the same starting scale.  Model: a step overflows exactly
-    when S >= 2^17.  GradScaler: 2000 clean + 1 skipped per cycle; the
-    hysteresis-2 policy: 1000 clean + 2 skipped per cycle."""
+    """The page's other comparison: moving a training setup from one policy
+    to the other changes how often steps are skipped, even from the same
+    starting scale.  Model: a step overflows exactly when S >= 2^17.
+    GradScaler: 2000 clean + 1 skipped per cycle; the hysteresis-2 policy:
+    1000 clean + 2 skipped per cycle."""
     def simulate(update, st, n):
         skips = 0
         for _ in range(n):
