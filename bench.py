@@ -139,16 +139,21 @@ def _time_launches(fn, reps, flush=None):
 def measure_configs(dev):
     """Per-configuration kernel timings outside the step: the tiny case, the
     8192x8192 per-tensor pair and the 4 GiB special-value tensors.  A 1 GiB
-    write evicts the 256 MB infinity cache before each timed launch."""
+    write and a 1 GiB read evict the 256 MB infinity cache before each timed
+    launch of the per-tensor pair."""
     import torch
 
     import loss_scaling_fp8_amd as gs
     import synth
 
     junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     def flush():
+        # a 1 GiB write then a 1 GiB read (stream-ordered): a cold cache that
+        # holds clean lines, so no write-back is charged to the timed launch
         junk.fill_(1.0)
+        junk_rd.sum()
 
     res = {}
     # tiny: 16 FP16 tensors (2^20 elements) unscale + update; 1024^2 per-tensor E4M3
@@ -162,6 +167,20 @@ def measure_configs(dev):
     torch.cuda.synchronize()
     ms, _ = _time_launches(lambda: (gs.gs_unscale_check(grads, outs, S, fi),
                                     gs.gs_update_scale(S, tr, fi, 2.0, 0.5, 2000)), 50)
+    # the same step captured in a HIP graph (the list is cached, so the
+    # calls allocate nothing): one replay per step removes the host launch cost
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gs.gs_unscale_check(grads, outs, S, fi)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        gs.gs_unscale_check(grads, outs, S, fi)
+        gs.gs_update_scale(S, tr, fi, 2.0, 0.5, 2000)
+    graph.replay()
+    torch.cuda.synchronize()
+    ms_graph, _ = _time_launches(graph.replay, 50)
     q = synth.tiny_quant()
     xq = q.full(dev)
     cq, sq = gs.fp8_quantize(xq, q.fmt, q.gran)
@@ -169,6 +188,7 @@ def measure_configs(dev):
     dq = gs.fp8_dequantize(cq, q.fmt, q.gran, sq)
     ms_d, _ = _time_launches(lambda: gs.fp8_dequantize(cq, q.fmt, q.gran, sq, dq), 50)
     res["tiny"] = {"unscale+update_us_per_step": round(ms * 1e3, 2),
+                   "unscale+update_us_per_step_hip_graph": round(ms_graph * 1e3, 2),
                    "quant_per_tensor_1024x1024_us": round(ms_q * 1e3, 2),
                    "dequant_1024x1024_us": round(ms_d * 1e3, 2),
                    "note": "launch-bound and cache-resident: correctness case, no GB/s claim"}

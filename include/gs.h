@@ -12,7 +12,9 @@
  * call of gs_unscale_check / gs_unscale_check_sumsq with a new gradient
  * list: it allocates the list's chunk descriptors and uploads them with a
  * blocking copy (and evicting an old list from the cache waits for the
- * device); repeated calls with the same list do neither.
+ * device); repeated calls with the same list do neither.  After that first
+ * call every entry point can be captured in a HIP graph: none allocates,
+ * copies from the host or records a memset.
  *
  * Errors: argument errors are detected on the host and returned before
  * anything is enqueued, with no side effects.  Non-finite DATA is never an

@@ -1,0 +1,178 @@
+"""GPU checks of the boundary's own machinery, through the C ABI against the
+oracle: the device cache of gradient-list descriptors under eviction, calls
+from several host threads on their own streams, and a whole step captured in
+a HIP graph (after the list's first call, the library allocates nothing and
+records no memset), replayed with eager work between the replays."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import loss_scaling_fp8_amd as gs
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda:0")
+
+
+def _to_dev(h, dev):
+    return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.float16).to(dev)
+
+
+def _bits(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def _random_f16(rng, n):
+    h = rng.integers(0, 0x7C00, size=n, dtype=np.uint32).astype(np.uint16)
+    return h | (rng.integers(0, 2, size=n).astype(np.uint16) << 15)
+
+
+def test_descriptor_cache_eviction(dev):
+    """80 distinct lists (the cache keeps 64): every call, including the
+    repeat of an evicted list, matches the oracle."""
+    rng = np.random.default_rng(81)
+    lists = []
+    for k in range(80):
+        sizes = [int(v) for v in rng.integers(1, 5000, size=3)]
+        host = [_random_f16(rng, n) for n in sizes]
+        lists.append((host, [_to_dev(h, dev) for h in host],
+                      [torch.empty(n, dtype=torch.float32, device=dev) for n in sizes]))
+    S = torch.tensor([256.0], dtype=torch.float32, device=dev)
+    for rnd in range(2):                    # the second round repeats lists evicted in the first
+        for k in (list(range(80)) if rnd == 0 else [0, 1, 2, 79, 40, 0]):
+            host, g, o = lists[k]
+            f = torch.zeros(1, dtype=torch.int32, device=dev)
+            for out in o:
+                out.fill_(-1.0)
+            gs.gs_unscale_check(g, o, S, f)
+            ref, rf = oracle.unscale_check(host, 256.0)
+            torch.cuda.synchronize()
+            for out, r in zip(o, ref):
+                assert np.array_equal(_bits(out), r.view(np.uint32)), (rnd, k)
+            assert int(f.item()) == rf
+
+
+def test_concurrent_host_threads_on_own_streams(dev):
+    """Four host threads, each with its own stream and gradient list, call
+    the unscale and the quantizer 25 times; every result matches the oracle
+    (the descriptor cache is shared and locked)."""
+    rng = np.random.default_rng(82)
+    work = []
+    for t in range(4):
+        host = [_random_f16(rng, n) for n in (3000 + t, 77, 20000)]
+        xq = (rng.standard_normal((64, 256)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        work.append((host, xq))
+    errors = []
+
+    def run(t):
+        try:
+            host, xq = work[t]
+            s = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(s):
+                g = [_to_dev(h, dev) for h in host]
+                o = [torch.empty(h.size, dtype=torch.float32, device=dev) for h in host]
+                x = torch.from_numpy(xq.view(np.int16)).view(torch.bfloat16).to(dev)
+                S = torch.tensor([1024.0], dtype=torch.float32, device=dev)
+                f = torch.zeros(1, dtype=torch.int32, device=dev)
+                for _ in range(25):
+                    gs.gs_unscale_check(g, o, S, f)
+                    codes, scales = gs.fp8_quantize(x, gs.FP8_E4M3, gs.FP8_BLOCK_1x128)
+                s.synchronize()
+                ref, _ = oracle.unscale_check(host, 1024.0)
+                for out, r in zip(o, ref):
+                    assert np.array_equal(_bits(out), r.view(np.uint32))
+                rc, rs, _ = oracle.quantize(xq, gs.FP8_E4M3, gs.FP8_BLOCK_1x128)
+                assert np.array_equal(codes.cpu().numpy(), rc)
+                assert np.array_equal(scales.cpu().numpy().reshape(-1).view(np.uint32), rs.view(np.uint32))
+        except Exception as e:          # noqa: BLE001 -- reported below
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=run, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+
+
+def test_step_captured_in_a_hip_graph(dev):
+    """unscale + check, update, 1x128 quantize and dequantize captured once
+    (the list is cached by an eager call first) and replayed 6 times; an Inf
+    is written eagerly into the input before replay 3 and removed after it;
+    every replay matches the oracle (outputs, flag consumed, S / tracker /
+    skips, codes, scales, dequantized values)."""
+    g = synth.tiny_gradset()
+    host = [synth.as_u16_numpy(synth.to_f16_tensor(g.gen(t, torch.arange(sp.numel))))
+            for t, sp in enumerate(g.tensors)]
+    grads = [_to_dev(h, dev) for h in host]
+    outs = [torch.empty(h.size, dtype=torch.float32, device=dev) for h in host]
+    q = synth.QuantSpec("graph", 256, 512, 0, 1, 7, 7, "gauss", 1.0, 0.01, 300.0)
+    bits = q.gen(torch.arange(256 * 512)).to(torch.int32).to(torch.int16)
+    xh = bits.numpy().view(np.uint16).reshape(256, 512)
+    x = bits.view(torch.bfloat16).reshape(256, 512).to(dev)
+    codes = torch.empty((256, 512), dtype=torch.uint8, device=dev)
+    scales = torch.empty(gs.scale_shape(256, 512, gs.FP8_BLOCK_1x128), dtype=torch.float32, device=dev)
+    deq = torch.empty((256, 512), dtype=torch.float32, device=dev)
+    S = torch.tensor([g.scale], dtype=torch.float32, device=dev)
+    tracker = torch.zeros(1, dtype=torch.int32, device=dev)
+    found = torch.zeros(1, dtype=torch.int32, device=dev)
+    skips = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def step():
+        gs.gs_unscale_check(grads, outs, S, found)
+        gs.gs_update_scale(S, tracker, found, 2.0, 0.5, 4, skips)
+        gs.fp8_quantize(x, gs.FP8_E4M3, gs.FP8_BLOCK_1x128, gs.FP8_SCALE_FROM_AMAX, codes, scales)
+        gs.fp8_dequantize(codes, gs.FP8_E4M3, gs.FP8_BLOCK_1x128, scales, deq)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # caches the descriptors, warms up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    S.fill_(g.scale)
+    tracker.zero_()
+    found.zero_()
+    skips.zero_()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    R = oracle.ScalerState(g.scale)
+    rc, rs, _ = oracle.quantize(xh, gs.FP8_E4M3, gs.FP8_BLOCK_1x128)
+    rd = oracle.dequantize(rc, gs.FP8_E4M3, gs.FP8_BLOCK_1x128, rs)
+    inj_t, inj_i = 5, 17
+    for r in range(1, 7):
+        if r == 3:
+            host[inj_t][inj_i] = 0x7C00
+            grads[inj_t][inj_i:inj_i + 1] = _to_dev(np.array([0x7C00], np.uint16), dev)
+        for o in outs:
+            o.fill_(-2.0)                         # eager work between replays
+        codes.zero_()
+        deq.zero_()
+        graph.replay()
+        ref, rf = oracle.unscale_check(host, float(R.S))
+        R.found_inf.value = rf
+        oracle.update_scale(R, 2.0, 0.5, 4)
+        torch.cuda.synchronize()
+        for o, rr in zip(outs, ref):
+            assert np.array_equal(_bits(o), rr.view(np.uint32)), r
+        assert (float(S.item()), int(tracker.item()), int(skips.item()), int(found.item())) == \
+            (float(R.S), R.tracker.value, R.skips.value, 0), r
+        assert np.array_equal(codes.cpu().numpy(), rc), r
+        assert np.array_equal(scales.cpu().numpy().reshape(-1).view(np.uint32), rs.view(np.uint32)), r
+        assert np.array_equal(deq.cpu().numpy().view(np.uint32), rd.view(np.uint32)), r
+        if r == 3:
+            orig = int(g.gen(inj_t, torch.tensor([inj_i]))[0]) & 0xFFFF
+            host[inj_t][inj_i] = orig
+            grads[inj_t][inj_i:inj_i + 1] = _to_dev(np.array([orig], np.uint16), dev)
+    # closed form: replays 1-2 clean, 3 skipped (S halves), 4-6 clean (tracker 3 < 4)
+    assert (float(R.S), R.skips.value, R.tracker.value) == (g.scale / 2, 1, 3)
