@@ -102,6 +102,27 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
                            int32_t *found_inf, void *stream);
 
 /*
+ * gs_unscale_list_descriptors -- the chunk descriptors gs_unscale_check
+ * builds for this gradient list, written to host memory (for inspection and
+ * tests; no HIP call, nothing on the device).  Chunk k of the list (tensors
+ * in order, empty ones contribute none, each cut into 2048-element chunks,
+ * its last chunk ragged) is two words:
+ *   desc_out[2k]     = address of the chunk's first FP16 input element
+ *                      | (element count << 48 when the chunk is ragged, else 0)
+ *   desc_out[2k + 1] = address of the chunk's first FP32 output element
+ *                      | 1 when the tensor's input or output address is not
+ *                      16-byte aligned (the element-wise path), else 0
+ *   grads, outs, numels  as gs_unscale_check (host arrays; the addresses are
+ *                        not dereferenced).
+ *   desc_out   host array of 2 * capacity words, or NULL to count only.
+ * Returns the number of chunks (>= 0), or a negative gs_status: argument
+ * errors as gs_unscale_check, GS_ERR_ARG when an address reaches 2^48,
+ * GS_ERR_SIZE when capacity is smaller than the count.
+ */
+int64_t gs_unscale_list_descriptors(int32_t n, const void *const *grads, float *const *outs,
+                                    const int64_t *numels, uint64_t *desc_out, int64_t capacity);
+
+/*
  * gs_unscale_check_sumsq_workspace_size -- bytes of device workspace
  * gs_unscale_check_sumsq needs for a list with these element counts:
  * 16 * (sum over tensors of ceil(numels[i] / 2048) + 1024).  Returns 0 for

@@ -23,7 +23,8 @@ FP8_E4M3, FP8_E5M2 = 0, 1
 FP8_PER_TENSOR, FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_BLOCK_1x32 = 0, 1, 2, 3
 FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 
-EXPORTS = ("gs_unscale_check", "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
+EXPORTS = ("gs_unscale_check", "gs_unscale_list_descriptors",
+           "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
            "gs_update_scale", "gs_update_scale_hysteresis", "fp8_quantize_workspace_size",
            "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "fp8_quantize_mx",
            "fp8_dequantize_mx", "gs_status_string")
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.gs_unscale_check.argtypes = [I32, P, P, P, ctypes.c_int, P, P, P]
         L.gs_unscale_check.restype = I32
+        L.gs_unscale_list_descriptors.argtypes = [I32, P, P, P, P, I64]
+        L.gs_unscale_list_descriptors.restype = I64
         L.gs_unscale_check_sumsq_workspace_size.argtypes = [I32, P]
         L.gs_unscale_check_sumsq_workspace_size.restype = ctypes.c_size_t
         L.gs_unscale_check_sumsq.argtypes = [I32, P, P, P, ctypes.c_int, P, P, P, P, P,

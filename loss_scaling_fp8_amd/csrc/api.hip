@@ -64,13 +64,14 @@ std::string make_key(int device, int32_t n, const void *const *in, float *const 
     return k;
 }
 
-gs_status build_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
-                     CachedList &cl) {
-    using gsk::ChunkDesc;
+// The chunk descriptors of a list, on the host (no HIP call).  GS_ERR_ARG
+// when an address reaches 2^48.
+gs_status make_descriptors(int32_t n, const void *const *in, float *const *out,
+                           const int64_t *numel, std::vector<gsk::ChunkDesc> &host) {
     using gsk::kUnscaleChunk;
     int64_t total = 0;
     for (int32_t i = 0; i < n; ++i) total += (numel[i] + kUnscaleChunk - 1) / kUnscaleChunk;
-    std::vector<ChunkDesc> host(static_cast<size_t>(total));
+    host.assign(static_cast<size_t>(total), gsk::ChunkDesc{0, 0});
     size_t k = 0;
     for (int32_t i = 0; i < n; ++i) {
         if (numel[i] == 0) continue;
@@ -88,7 +89,16 @@ gs_status build_list(int32_t n, const void *const *in, float *const *out, const 
             ++k;
         }
     }
-    const size_t bytes = host.size() * sizeof(ChunkDesc);
+    return GS_OK;
+}
+
+gs_status build_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
+                     CachedList &cl) {
+    std::vector<gsk::ChunkDesc> host;
+    const gs_status st = make_descriptors(n, in, out, numel, host);
+    if (st != GS_OK) return st;
+    const int64_t total = int64_t(host.size());
+    const size_t bytes = host.size() * sizeof(gsk::ChunkDesc);
     void *dev = nullptr;
     if (hipMalloc(&dev, bytes) != hipSuccess) return GS_ERR_HIP;
     if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
@@ -158,6 +168,24 @@ inline bool misaligned(const void *p, uintptr_t a) { return (uintptr_t(p) & (a -
 
 inline gs_status from_hip(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
 
+// Argument checks of a gradient list (pointers, counts, alignment); the
+// element total in *total.
+gs_status check_list(int32_t n, const void *const *grads, float *const *outs,
+                     const int64_t *numels, int64_t *total) {
+    *total = 0;
+    if (n < 0) return GS_ERR_SIZE;
+    if (n == 0) return GS_OK;
+    if (!grads || !outs || !numels) return GS_ERR_NULL;
+    for (int32_t i = 0; i < n; ++i) {
+        if (numels[i] < 0 || numels[i] > kMaxElems) return GS_ERR_SIZE;
+        if (numels[i] > 0 && (!grads[i] || !outs[i])) return GS_ERR_NULL;
+        if (misaligned(grads[i], 2) || misaligned(outs[i], 4)) return GS_ERR_ALIGN;
+        *total += numels[i];
+        if (*total > kMaxElems * 64) return GS_ERR_SIZE;
+    }
+    return GS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,16 +197,9 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
     if (in_dtype != GS_F16) return GS_ERR_DTYPE;
     if (!scale || !found_inf) return GS_ERR_NULL;
     if (misaligned(scale, 4) || misaligned(found_inf, 4)) return GS_ERR_ALIGN;
-    if (n == 0) return GS_OK;
-    if (!grads || !outs || !numels) return GS_ERR_NULL;
     int64_t total = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        if (numels[i] < 0 || numels[i] > kMaxElems) return GS_ERR_SIZE;
-        if (numels[i] > 0 && (!grads[i] || !outs[i])) return GS_ERR_NULL;
-        if (misaligned(grads[i], 2) || misaligned(outs[i], 4)) return GS_ERR_ALIGN;
-        total += numels[i];
-        if (total > kMaxElems * 64) return GS_ERR_SIZE;
-    }
+    const gs_status vs = check_list(n, grads, outs, numels, &total);
+    if (vs != GS_OK) return vs;
     if (total == 0) return GS_OK;
     CachedList cl;
     const gs_status st = get_list(n, grads, outs, numels, cl);
@@ -186,6 +207,25 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
     return from_hip(gsk::launch_unscale_check(static_cast<const gsk::ChunkDesc *>(cl.dev),
                                               cl.nchunks, scale, found_inf,
                                               static_cast<hipStream_t>(stream)));
+}
+
+int64_t gs_unscale_list_descriptors(int32_t n, const void *const *grads, float *const *outs,
+                                    const int64_t *numels, uint64_t *desc_out, int64_t capacity) {
+    int64_t total = 0;
+    gs_status st = check_list(n, grads, outs, numels, &total);
+    if (st != GS_OK) return st;
+    std::vector<gsk::ChunkDesc> host;
+    st = make_descriptors(n, grads, outs, numels, host);
+    if (st != GS_OK) return st;
+    const int64_t count = int64_t(host.size());
+    if (desc_out) {
+        if (capacity < count) return GS_ERR_SIZE;
+        for (int64_t k = 0; k < count; ++k) {
+            desc_out[2 * k] = host[size_t(k)].in_bits;
+            desc_out[2 * k + 1] = host[size_t(k)].out_bits;
+        }
+    }
+    return count;
 }
 
 size_t gs_unscale_check_sumsq_workspace_size(int32_t n, const int64_t *numels) {
@@ -208,15 +248,9 @@ gs_status gs_unscale_check_sumsq(int32_t n, const void *const *grads, float *con
     if (misaligned(scale, 4) || misaligned(found_inf, 4) || misaligned(sumsq, 8) ||
         misaligned(norm_sq, 8))
         return GS_ERR_ALIGN;
-    if (n > 0 && (!grads || !outs || !numels)) return GS_ERR_NULL;
     int64_t total = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        if (numels[i] < 0 || numels[i] > kMaxElems) return GS_ERR_SIZE;
-        if (numels[i] > 0 && (!grads[i] || !outs[i])) return GS_ERR_NULL;
-        if (misaligned(grads[i], 2) || misaligned(outs[i], 4)) return GS_ERR_ALIGN;
-        total += numels[i];
-        if (total > kMaxElems * 64) return GS_ERR_SIZE;
-    }
+    const gs_status vs = check_list(n, grads, outs, numels, &total);
+    if (vs != GS_OK) return vs;
     if (!workspace || workspace_bytes < gs_unscale_check_sumsq_workspace_size(n, numels))
         return GS_ERR_WORKSPACE;
     if (misaligned(workspace, 16)) return GS_ERR_ALIGN;

@@ -217,3 +217,74 @@ def test_mx_and_1x32_argument_errors():
     assert L.fp8_quantize(FAKE, 2, 4, 48, 0, 3, 0, FAKE, FAKE, None, None, 0, None) == -3
     assert L.fp8_dequantize(FAKE, 4, 48, 0, 3, FAKE, FAKE, None) == -3
     assert L.fp8_quantize(FAKE, 2, 4, 64, 0, 4, 0, FAKE, FAKE, None, None, 0, None) == -5
+
+
+def _descriptor_layout(ins, outs, numels):
+    """The documented chunk-descriptor layout of gs_unscale_list_descriptors."""
+    d = []
+    for a, b, n in zip(ins, outs, numels):
+        if n == 0:
+            continue
+        scalar = 1 if (a | b) & 15 else 0
+        for st in range(0, n, 2048):
+            left = n - st
+            ragged = left if left < 2048 else 0
+            d.append(((a + 2 * st) | (ragged << 48), (b + 4 * st) | scalar))
+    return d
+
+
+def _call_descriptors(ins, outs, numels, capacity=None, with_out=True):
+    L = gs.lib()
+    n = len(numels)
+    gi = (ctypes.c_void_p * max(n, 1))(*ins)
+    go = (ctypes.c_void_p * max(n, 1))(*outs)
+    nu = (ctypes.c_int64 * max(n, 1))(*numels)
+    cap = capacity if capacity is not None else sum((x + 2047) // 2048 for x in numels)
+    buf = (ctypes.c_uint64 * max(2 * cap, 2))()
+    r = L.gs_unscale_list_descriptors(n, gi, go, nu, buf if with_out else None, cap)
+    return r, [(buf[2 * k], buf[2 * k + 1]) for k in range(max(r, 0))] if with_out else None
+
+
+def test_list_descriptors_layout():
+    """The host-side chunking of the multi-tensor unscale: tensors in order,
+    empty ones skipped, 2048-element chunks, the ragged count of each last
+    chunk in bits 48-63, the element-wise flag for tensors whose input or
+    output is not 16-byte aligned."""
+    import random
+    rnd = random.Random(5)
+    sizes = [0, 1, 7, 2047, 2048, 2049, 4096, 6149, 0, 1_000_003, 65536, 3]
+    # per-tensor bases 1 GiB apart, offset in 2-byte (input) and 4-byte
+    # (output) steps: some tensors 16-byte aligned on both sides, some not
+    ins = [(1 << 40) + (k << 30) + (0 if k % 2 == 0 else 2 * (k % 8)) for k in range(len(sizes))]
+    outs = [(1 << 42) + (k << 31) + (0 if k % 2 == 0 else 4 * (1 + k % 3)) for k in range(len(sizes))]
+    r, got = _call_descriptors(ins, outs, sizes)
+    want = _descriptor_layout(ins, outs, sizes)
+    assert r == len(want) == sum((n + 2047) // 2048 for n in sizes)
+    assert got == want
+    assert any(o & 1 for _, o in want) and any(not (o & 1) for _, o in want)
+    # the count alone, and its agreement with the sum-of-squares workspace size
+    r2, _ = _call_descriptors(ins, outs, sizes, with_out=False)
+    assert r2 == r == gs.gs_unscale_check_sumsq_workspace_size(sizes) // 16 - 1024
+    # random lists
+    for trial in range(20):
+        m = rnd.randint(1, 30)
+        ns = [rnd.choice([0, rnd.randint(1, 5000), rnd.randint(1, 300000)]) for _ in range(m)]
+        ii = [(1 << 40) + 2 * rnd.randint(0, 1 << 30) for _ in ns]
+        oo = [(1 << 41) + 4 * rnd.randint(0, 1 << 30) for _ in ns]
+        assert _call_descriptors(ii, oo, ns)[1] == _descriptor_layout(ii, oo, ns)
+
+
+def test_list_descriptors_errors():
+    # capacity smaller than the count
+    r, _ = _call_descriptors([FAKE], [FAKE], [5000], capacity=2)
+    assert r == -2
+    # an address reaching 2^48
+    r, _ = _call_descriptors([(1 << 48) - 64], [FAKE], [100])
+    assert r == -5
+    r, _ = _call_descriptors([FAKE], [(1 << 48) - 128], [100])
+    assert r == -5
+    # alignment to the element size, negative counts, empty list
+    assert _call_descriptors([FAKE + 1], [FAKE], [10])[0] == -6
+    assert _call_descriptors([FAKE], [FAKE + 2], [10])[0] == -6
+    assert _call_descriptors([FAKE], [FAKE], [-1])[0] == -2
+    assert _call_descriptors([], [], [])[0] == 0
