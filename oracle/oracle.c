@@ -57,6 +57,13 @@
  * and the skip count) have no value on the pages to check against; they are
  * pinned only by rule-level unit tests of this file's own behaviour.  Every
  * function's finite-data behaviour is pinned externally (see the tests).
+ * Partly unpinned for the same reason: the window maximum of delayed
+ * scaling (pinned by its reduction to per-tensor scaling and the window's
+ * closed form), the knob semantics of the second scaler policy (pinned by
+ * its reduction to the GradScaler policy, closed forms and the page's two
+ * comparisons), and the power-of-two rule of the MX scale (pinned by the
+ * listing with that rule applied, the exponent-field identity and the
+ * no-saturation property).
  */
 #include <math.h>
 #include <stdint.h>
