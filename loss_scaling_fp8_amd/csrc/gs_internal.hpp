@@ -10,6 +10,32 @@
 
 namespace gsk {
 
+// ---------------------------------------------------------------- stores
+// A 16-byte store with a chosen cache policy.  POLICY < 0 is an ordinary
+// global store (-1 non-temporal, -2 plain); POLICY >= 0 is the policy field
+// of a buffer store (gfx950: sc0 = 1, nt = 2, sc1 = 16), through a buffer
+// resource at the wave-uniform address `base`; `off` is the lane's byte
+// offset from `base`, any size for the global stores, below 2^31 for the
+// buffer store (the resource's range is 2^31 - 1 bytes).
+constexpr int kPolicyGlobalNt = -1;
+constexpr int kPolicyGlobalPlain = -2;
+typedef uint32_t st_u32x4 __attribute__((ext_vector_type(4)));
+
+template <int POLICY, typename V>
+__device__ __forceinline__ void store16(void *base, int64_t off, V v) {
+    static_assert(sizeof(V) == 16, "16-byte stores only");
+    const st_u32x4 w = __builtin_bit_cast(st_u32x4, v);
+    if constexpr (POLICY == kPolicyGlobalNt) {
+        __builtin_nontemporal_store(w, reinterpret_cast<st_u32x4 *>(static_cast<char *>(base) + off));
+    } else if constexpr (POLICY == kPolicyGlobalPlain) {
+        *reinterpret_cast<st_u32x4 *>(static_cast<char *>(base) + off) = w;
+    } else {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, POLICY);
+    }
+}
+
 // ---------------------------------------------------------------- unscale
 // The gradient list is cut into chunks of kUnscaleChunk elements (the last
 // chunk of a tensor ragged), and each chunk gets a 16-byte descriptor built

@@ -29,6 +29,15 @@
 
 #include <atomic>
 
+// Store policy of the outputs (see store16): device-scope non-temporal
+// (sc1 nt).  On the Llama-3-8B set, ten launches back to back ran 1.3%
+// faster than with plain non-temporal stores, and the benchmark step (the
+// 1x128 quantize runs next) 0.6% faster.  The dequantizers keep plain
+// non-temporal stores: with sc1 their writes drain into the next kernel
+// (back to back they ran 16-19% slower).
+#ifndef GS_UNSCALE_STORE
+#define GS_UNSCALE_STORE 18
+#endif
 #ifndef GS_UNSCALE_GRID_CAP
 #define GS_UNSCALE_GRID_CAP (1 << 22)
 #endif
@@ -118,7 +127,6 @@ void unscale_check_kernel(const ChunkDesc *__restrict__ descs, int64_t nchunks,
         uint64_t hib = 0;                    // SUMSQ: sum of bits(t) - bits(C)
         if (ragged == 0 && (d.out_bits & 1) == 0) {
             g_cu32x2 *src = (g_cu32x2 *)in;
-            g_f32x4 *dst = (g_f32x4 *)out;
             u32x2 v[kUnscaleUnroll];
 #pragma unroll
             for (int u = 0; u < kUnscaleUnroll; ++u) v[u] = src[u * kUnscaleThreads + tid];
@@ -129,7 +137,8 @@ void unscale_check_kernel(const ChunkDesc *__restrict__ descs, int64_t nchunks,
                 const float f2 = widen_f16(v[u].y & 0xFFFFu), f3 = widen_f16(v[u].y >> 16);
                 const f32x4 y = {unscale_f(f0, inv, bad), unscale_f(f1, inv, bad),
                                  unscale_f(f2, inv, bad), unscale_f(f3, inv, bad)};
-                __builtin_nontemporal_store(y, &dst[u * kUnscaleThreads + tid]);
+                store16<GS_UNSCALE_STORE>((void *)(uintptr_t)(d.out_bits & ~uint64_t(3)),
+                                          uint32_t(u * kUnscaleThreads + tid) * 16u, y);
                 if (SUMSQ) {
                     sq_add(f0, lo, hib);
                     sq_add(f1, lo, hib);
