@@ -68,7 +68,7 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
     core, then with the sample split into independent pieces (gradient
     chunks; activation row groups; 128-row weight groups, so no block is
     split) run by a thread pool over the host's cores (the C calls release
-    the GIL).  The all-cores figure is the value."""
+    the GIL), three times.  The median of the all-cores runs is the value."""
     import os
     from concurrent.futures import ThreadPoolExecutor
 
@@ -100,15 +100,19 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
     except AttributeError:
         ncpu = os.cpu_count() or 1
     threads = max(1, min(16, ncpu))
-    t0 = time.perf_counter()
+    runs = []
     with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(lambda j: j[0](*j[1]), jobs))
-    t_all = time.perf_counter() - t0
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(lambda j: j[0](*j[1]), jobs))
+            runs.append(time.perf_counter() - t0)
+    t_all = float(np.median(runs))
     return {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "value_1_core": round(nbytes / t_one / 1e9, 4),
             "sample": "%d FP16 elements (embedding + lm_head gradients) unscaled, %dx%d "
                       "activation rows 1x128 and %dx%d weight rows 128x128 quantized and "
-                      "dequantized, E4M3; the C oracle on %d threads (%.1f s) and on 1 (%.1f s)"
+                      "dequantized, E4M3; the C oracle on %d threads (median of 3 runs, "
+                      "%.1f s) and on 1 (%.1f s)"
                       % (grad_sample.size, act_rows.shape[0], act_rows.shape[1],
                          wgt_rows.shape[0], wgt_rows.shape[1], threads, t_all, t_one)}
 
