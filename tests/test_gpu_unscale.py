@@ -71,7 +71,8 @@ def test_tiny_gradset_50_step_trajectory(dev):
 
 
 SCALES = [2.0 ** k for k in range(-20, 41, 3)] + [3.0, 1000.0, 1e-30, 7e-39, 1e-45, 3.0e38,
-                                                  float("inf"), 0.0]
+                                                  float("inf"), 0.0, float("nan"),
+                                                  float("-inf"), -0.0, -2.0, -3.0e38]
 
 
 def test_every_fp16_pattern_times_scales(dev):
@@ -193,3 +194,30 @@ def test_abi_errors_leave_no_side_effects(dev):
         gs.gs_unscale_check([g.float()], [o], S, f)
     torch.cuda.synchronize()
     assert float(S.item()) == 1.0 and int(f.item()) == 0
+
+
+@pytest.mark.parametrize("S0", [0.0, float("inf"), float("-inf"), float("nan"), -0.0, -4.0,
+                                3.0e38, 1e-45])
+def test_forced_scale_states_step_by_step(dev, S0):
+    """The loop forced into a degenerate state: S = 0, +-Inf, NaN, -0, a
+    negative or a huge or a subnormal value, then 6 steps of unscale + update
+    (one clean gradient list, growth interval 2).  Every step's outputs, flag
+    and state match the oracle bit for bit."""
+    rng = np.random.default_rng(77)
+    host = [rng.integers(0, 0x7C00, size=n, dtype=np.uint32).astype(np.uint16) for n in (5, 3000)]
+    grads = [_to_dev(h, dev) for h in host]
+    outs = [torch.empty(h.size, dtype=torch.float32, device=dev) for h in host]
+    D = DevScaler(S0, dev)
+    R = oracle.ScalerState(S0)
+    for step in range(6):
+        gs.gs_unscale_check(grads, outs, D.S, D.found)
+        ref, R.found_inf.value = oracle.unscale_check(host, float(R.S), R.found_inf.value)
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert np.array_equal(_bits(o), r.view(np.uint32)), (S0, step)
+        assert int(D.found.item()) == R.found_inf.value, (S0, step)
+        gs.gs_update_scale(D.S, D.tracker, D.found, 2.0, 0.5, 2, D.skips)
+        oracle.update_scale(R, 2.0, 0.5, 2)
+        S, t, f, k = D.state()
+        assert np.float32(S).view(np.uint32) == R.S.view(np.uint32), (S0, step)
+        assert (t, f, k) == (R.tracker.value, 0, R.skips.value), (S0, step)
