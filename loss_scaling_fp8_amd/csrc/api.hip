@@ -26,11 +26,14 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 // Key: device id + the (input, output, numel) triplets.  Value: one device
 // allocation holding the per-chunk descriptors.  Least-recently-used
 // eviction by count and by bytes; an evicted list may still be referenced by
-// queued kernels, so eviction waits for the device before freeing.
+// queued kernels, so eviction waits for the list's device before freeing.
+// A caller enqueues its kernel while holding the cache lock (with_list), so
+// no list can be evicted between its lookup and the launch that reads it.
 struct CachedList {
     void *dev = nullptr;
     int64_t nchunks = 0;
     size_t bytes = 0;
+    int device = 0;
 };
 
 constexpr size_t kCacheEntries = 64;
@@ -111,8 +114,20 @@ gs_status build_list(int32_t n, const void *const *in, float *const *out, const 
     return GS_OK;
 }
 
-gs_status get_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
-                   CachedList &result) {
+// Frees an evicted list once its device has finished the work queued so far
+// (every kernel that reads it was enqueued under the cache lock, before this).
+void free_list(const CachedList &cl, int current_device) {
+    if (cl.device != current_device) (void)hipSetDevice(cl.device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(cl.dev);
+    if (cl.device != current_device) (void)hipSetDevice(current_device);
+}
+
+// Looks up (or builds and caches) the list's descriptors and calls
+// launch(list) with the cache lock held.
+template <typename F>
+gs_status with_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
+                    F &&launch) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return GS_ERR_HIP;
     std::string key = make_key(device, n, in, out, numel);
@@ -121,16 +136,15 @@ gs_status get_list(int32_t n, const void *const *in, float *const *out, const in
     auto it = c.map.find(key);
     if (it != c.map.end()) {
         c.lru.splice(c.lru.begin(), c.lru, it->second.second);
-        result = it->second.first;
-        return GS_OK;
+        return launch(static_cast<const CachedList &>(it->second.first));
     }
     CachedList cl;
     const gs_status st = build_list(n, in, out, numel, cl);
     if (st != GS_OK) return st;
+    cl.device = device;
     while (!c.lru.empty() && (c.map.size() >= kCacheEntries || c.bytes + cl.bytes > kCacheBytes)) {
         auto oit = c.map.find(c.lru.back());
-        (void)hipDeviceSynchronize();        // queued kernels may still read it
-        (void)hipFree(oit->second.first.dev);
+        free_list(oit->second.first, device);
         c.bytes -= oit->second.first.bytes;
         c.map.erase(oit);
         c.lru.pop_back();
@@ -138,8 +152,7 @@ gs_status get_list(int32_t n, const void *const *in, float *const *out, const in
     c.lru.push_front(key);
     c.map.emplace(key, std::make_pair(cl, c.lru.begin()));
     c.bytes += cl.bytes;
-    result = cl;
-    return GS_OK;
+    return launch(static_cast<const CachedList &>(cl));
 }
 
 inline bool bad_enum_fmt(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
@@ -201,12 +214,11 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
     const gs_status vs = check_list(n, grads, outs, numels, &total);
     if (vs != GS_OK) return vs;
     if (total == 0) return GS_OK;
-    CachedList cl;
-    const gs_status st = get_list(n, grads, outs, numels, cl);
-    if (st != GS_OK) return st;
-    return from_hip(gsk::launch_unscale_check(static_cast<const gsk::ChunkDesc *>(cl.dev),
-                                              cl.nchunks, scale, found_inf,
-                                              static_cast<hipStream_t>(stream)));
+    return with_list(n, grads, outs, numels, [&](const CachedList &cl) {
+        return from_hip(gsk::launch_unscale_check(static_cast<const gsk::ChunkDesc *>(cl.dev),
+                                                  cl.nchunks, scale, found_inf,
+                                                  static_cast<hipStream_t>(stream)));
+    });
 }
 
 int64_t gs_unscale_list_descriptors(int32_t n, const void *const *grads, float *const *outs,
@@ -254,14 +266,13 @@ gs_status gs_unscale_check_sumsq(int32_t n, const void *const *grads, float *con
     if (!workspace || workspace_bytes < gs_unscale_check_sumsq_workspace_size(n, numels))
         return GS_ERR_WORKSPACE;
     if (misaligned(workspace, 16)) return GS_ERR_ALIGN;
-    CachedList cl;
-    if (total > 0) {
-        const gs_status st = get_list(n, grads, outs, numels, cl);
-        if (st != GS_OK) return st;
-    }
-    return from_hip(gsk::launch_unscale_check_sumsq(
-        static_cast<const gsk::ChunkDesc *>(cl.dev), cl.nchunks, scale, found_inf, sumsq, norm_sq,
-        workspace, static_cast<hipStream_t>(stream)));
+    auto launch = [&](const CachedList &cl) {
+        return from_hip(gsk::launch_unscale_check_sumsq(
+            static_cast<const gsk::ChunkDesc *>(cl.dev), cl.nchunks, scale, found_inf, sumsq,
+            norm_sq, workspace, static_cast<hipStream_t>(stream)));
+    };
+    if (total == 0) return launch(CachedList{});   // still folds the total into norm_sq
+    return with_list(n, grads, outs, numels, launch);
 }
 
 gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_inf,
