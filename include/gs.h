@@ -16,6 +16,13 @@
  * call every entry point can be captured in a HIP graph: none allocates,
  * copies from the host or records a memset.
  *
+ * Threads: entry points may be called from several host threads at once
+ * (each on its own stream, or the same one).  The descriptor cache is
+ * locked, and an unscale call enqueues its kernel while holding that lock,
+ * so no thread's eviction can free a list between another thread's lookup
+ * and its launch.  Calls whose device outputs or workspaces overlap must be
+ * ordered by the caller (streams or events), as for any asynchronous work.
+ *
  * Errors: argument errors are detected on the host and returned before
  * anything is enqueued, with no side effects.  Non-finite DATA is never an
  * error; it is reported through the found_inf / nonfinite flags.  A failing
