@@ -37,10 +37,17 @@ def log(*a):
 
 
 def kernel_source_hash(files):
+    """First 16 hex digits of the sha256 of the kernel sources' code: comments
+    and whitespace are removed first, so that editing prose does not detach
+    the committed counters from the kernel they were taken on."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "loss_scaling_fp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "loss_scaling_fp8_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

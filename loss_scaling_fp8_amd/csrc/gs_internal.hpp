@@ -30,6 +30,8 @@ __device__ __forceinline__ void store16(void *base, int64_t off, V v) {
     } else if constexpr (POLICY == kPolicyGlobalPlain) {
         *reinterpret_cast<st_u32x4 *>(static_cast<char *>(base) + off) = w;
     } else {
+        // raw (stride 0) resource; its last word sets the data-format field to
+        // 32 bits (4 << 15), which gfx9-family buffer accesses need non-zero
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
         __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, POLICY);
