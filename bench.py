@@ -279,8 +279,8 @@ def main():
                          "final-state readback, no CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU path only: --gpus must be 1 "
-              "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
+        print("bench.py measures the single-GPU path only: --gpus must be 1 (sharding across "
+              "GPUs is described in the design notes and not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -162,7 +162,7 @@ def test_ordinary_channel_error_independent_of_outlier():
 
 
 # ---------------------------------------------------------------- reading-defined rules
-# (The pages do not cover these; they are definitions of this build, checked
+# (The pages do not cover these; they are readings the oracle defines, checked
 # here for internal consistency only.)
 def test_special_values_rules():
     f32 = np.float32
