@@ -131,6 +131,8 @@ def lib() -> ctypes.CDLL:
             L.orc_dequantize_mx.argtypes = [P, I64, I64, ctypes.c_int, P, P]
             L.orc_dequantize_mx.restype = ctypes.c_int
             L.orc_dequantize.restype = ctypes.c_int
+            L.orc_dequantize_bf16.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P]
+            L.orc_dequantize_bf16.restype = ctypes.c_int
             L.orc_fp8_encode_array.argtypes = [P, I64, ctypes.c_int, P]
             L.orc_fp8_encode_array.restype = None
             L.orc_cast_array.argtypes = [P, I64, F, ctypes.c_int, P]
@@ -378,6 +380,21 @@ def dequantize(codes: np.ndarray, fmt: int, gran: int, scales: np.ndarray) -> np
     sc = np.ascontiguousarray(scales, np.float32).reshape(-1)
     out = np.empty((rows, cols), np.float32)
     rc = lib().orc_dequantize(_ptr(codes), rows, cols, fmt, gran, _ptr(sc), _ptr(out))
+    if rc != 0:
+        raise ValueError("shape %dx%d not divisible into blocks" % (rows, cols))
+    return out
+
+
+def dequantize_bf16(codes: np.ndarray, fmt: int, gran: int, scales: np.ndarray) -> np.ndarray:
+    """dequantize() rounded once more to BF16 (nearest, ties to even; NaN ->
+    0x7FC0).  Returns BF16 bit patterns, uint16 [rows, cols]."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    rows, cols = codes.shape
+    sc = np.ascontiguousarray(scales, np.float32).reshape(-1)
+    out = np.empty((rows, cols), np.uint16)
+    rc = lib().orc_dequantize_bf16(_ptr(codes), rows, cols, fmt, gran, _ptr(sc), _ptr(out))
+    if rc == -2:
+        raise MemoryError("oracle scratch allocation failed")
     if rc != 0:
         raise ValueError("shape %dx%d not divisible into blocks" % (rows, cols))
     return out

@@ -66,6 +66,7 @@
  * no-saturation property).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -79,6 +80,7 @@ enum { ORC_FROM_AMAX = 0, ORC_GIVEN = 1 };
 /* ------------------------------------------------------------------ */
 /* Bit-level helpers (memcpy: no aliasing games). */
 static float f32_of_bits(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+static uint32_t bits_of_f32(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
 
 static const uint32_t CANONICAL_NAN = 0x7FC00000u;
 
@@ -478,6 +480,39 @@ int orc_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
             out[r * cols + c] = isnan(o) ? f32_of_bits(CANONICAL_NAN) : o;
         }
     return 0;
+}
+
+/* Dequantize to BF16: the FP32 result of orc_dequantize rounded once more,
+ * to the nearest BF16 value with ties to an even last bit (the FP32 value
+ * cast to the BF16 compute type); NaN -> 0x7FC0.  BF16 keeps FP32's sign and
+ * exponent fields and the top 7 fraction bits, so the rounding acts on the
+ * low 16 bits of the FP32 pattern: drop them, and add one unit when they are
+ * above half a unit, or exactly half with the kept last bit odd (a carry
+ * moves into the exponent, giving Inf past the largest BF16). */
+static uint16_t bf16_rne(float y)
+{
+    if (isnan(y))
+        return 0x7FC0;
+    uint32_t b = bits_of_f32(y);
+    uint32_t kept = b >> 16, dropped = b & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        ++kept;
+    return (uint16_t)kept;
+}
+
+int orc_dequantize_bf16(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
+                        int gran, const float *scales, uint16_t *out)
+{
+    const int64_t n = rows * cols;
+    float *f32 = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!f32)
+        return -2;
+    int rc = orc_dequantize(codes, rows, cols, fmt, gran, scales, f32);
+    if (rc == 0)
+        for (int64_t i = 0; i < n; ++i)
+            out[i] = bf16_rne(f32[i]);
+    free(f32);
+    return rc;
 }
 
 /* MX-style blocks ("Mixed precision and FP8 training", hardware notes: MX

@@ -56,12 +56,15 @@ MUTANTS = {
     "block_1x32_as_1x64": ("{ *br = 1; *bc = 32; }", "{ *br = 1; *bc = 64; }"),
     "mx_nan_byte_ignored": ("b == 0xFF ? f32_of_bits(CANONICAL_NAN) : ", ""),
     "nan_input_unsigned": ("return (uint8_t)((signbit(f) ? 0x80 : 0x00) | 0x7F);", "return 0x7F;"),
+    "bf16_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))",
+                       "if (dropped >= 0x8000u)"),
+    "bf16_truncates": ("        ++kept;\n    return (uint16_t)kept;", "    return (uint16_t)kept;"),
 }
 
 FAST_PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_unscale.py",
              "tests/test_oracle_quant.py", "tests/test_oracle_delayed.py",
              "tests/test_oracle_sumsq.py", "tests/test_oracle_hysteresis.py",
-             "tests/test_oracle_mx.py"]
+             "tests/test_oracle_mx.py", "tests/test_oracle_bf16.py"]
 
 
 def _run_mutant(name, tmp_dir):
