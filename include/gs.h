@@ -328,6 +328,20 @@ gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_f
                          fp8_granularity g, const float *scales, float *out, void *stream);
 
 /*
+ * fp8_dequantize_bf16 -- the same value in the BF16 compute type: fl32(
+ * decode(code) * s) as fp8_dequantize computes it, then rounded to the
+ * nearest BF16 value with ties to an even last bit (a value past the largest
+ * BF16 becomes +-Inf); NaN is written as 0x7FC0.  The pages multiply by the
+ * scale in FP32 ("Mixed precision and FP8 training", quant()); the second
+ * rounding is this library's reading of handing that value to BF16 compute.
+ *   codes, scales, shapes and granularities as fp8_dequantize;
+ *   out        device BF16 bit patterns (uint16) rows x cols, 16-byte aligned.
+ */
+gs_status fp8_dequantize_bf16(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
+                              fp8_granularity g, const float *scales, uint16_t *out,
+                              void *stream);
+
+/*
  * fp8_quantize_mx -- MX-style quantization: 1x32 blocks along each row, one
  * power-of-two scale per block stored as an E8M0 byte ("Mixed precision and
  * FP8 training", hardware notes: the MX formats keep one scaling factor per

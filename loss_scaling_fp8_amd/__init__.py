@@ -26,8 +26,8 @@ FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 EXPORTS = ("gs_unscale_check", "gs_unscale_list_descriptors",
            "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
            "gs_update_scale", "gs_update_scale_hysteresis", "fp8_quantize_workspace_size",
-           "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "fp8_quantize_mx",
-           "fp8_dequantize_mx", "gs_status_string")
+           "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "fp8_dequantize_bf16",
+           "fp8_quantize_mx", "fp8_dequantize_mx", "gs_status_string")
 
 _lib = None
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_quantize_delayed.restype = I32
         L.fp8_dequantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P]
         L.fp8_dequantize.restype = I32
+        L.fp8_dequantize_bf16.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P]
+        L.fp8_dequantize_bf16.restype = I32
         L.fp8_quantize_mx.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, P, P, P, P]
         L.fp8_quantize_mx.restype = I32
         L.fp8_dequantize_mx.argtypes = [P, I64, I64, ctypes.c_int, P, P, P]
@@ -270,6 +272,20 @@ def fp8_dequantize(codes, fmt: int, gran: int, scales, out=None, stream=None):
         out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
     _check(lib().fp8_dequantize(_ptr(codes), rows, cols, int(fmt), int(gran), _ptr(scales),
                                 _ptr(out), _stream(stream)), "fp8_dequantize")
+    return out
+
+
+def fp8_dequantize_bf16(codes, fmt: int, gran: int, scales, out=None, stream=None):
+    """decode(code) * s in float32, rounded to bfloat16 (nearest, ties to
+    even); returns out [rows, cols] (torch.bfloat16)."""
+    import torch
+    if codes.dim() != 2 or codes.dtype != torch.uint8:
+        raise TypeError("codes must be a 2-D uint8 tensor")
+    rows, cols = codes.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().fp8_dequantize_bf16(_ptr(codes), rows, cols, int(fmt), int(gran), _ptr(scales),
+                                     _ptr(out), _stream(stream)), "fp8_dequantize_bf16")
     return out
 
 

@@ -382,6 +382,20 @@ gs_status fp8_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, fp8_f
                                            static_cast<hipStream_t>(stream)));
 }
 
+gs_status fp8_dequantize_bf16(const uint8_t *codes, int64_t rows, int64_t cols, fp8_format fmt,
+                              fp8_granularity g, const float *scales, uint16_t *out,
+                              void *stream) {
+    if (bad_enum_fmt(fmt) || bad_enum_gran(g)) return GS_ERR_ARG;
+    gs_status st = check_shape(rows, cols, g);
+    if (st != GS_OK) return st;
+    const int64_t n = rows * cols;
+    if (n > 0 && (!codes || !out || !scales)) return GS_ERR_NULL;
+    if (misaligned(codes, 16) || misaligned(out, 16) || misaligned(scales, 4)) return GS_ERR_ALIGN;
+    if (n == 0) return GS_OK;
+    return from_hip(gsk::launch_dequantize_bf16(codes, rows, cols, fmt, g, scales, out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 gs_status fp8_quantize_mx(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
                           fp8_format fmt, uint8_t *codes, uint8_t *scales_e8m0,
                           int32_t *nonfinite, void *stream) {

@@ -95,5 +95,8 @@ hipError_t launch_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols
                                 const uint8_t *scales, float *out, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
                              const float *scales, float *out, hipStream_t stream);
+hipError_t launch_dequantize_bf16(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
+                                  int gran, const float *scales, uint16_t *out,
+                                  hipStream_t stream);
 
 }  // namespace gsk

@@ -38,6 +38,7 @@
 //  * The max-abs is taken on bit patterns: for non-negative floats unsigned
 //    integer order is numeric order, and BF16 halves are maxed pairwise.
 #include "device_fp8.hpp"
+#include <hip/hip_bf16.h>
 #include "gs_internal.hpp"
 
 // Cache policy per kernel (1 = non-temporal), chosen by measurement.
@@ -540,17 +541,31 @@ void delayed_update_kernel(const uint32_t *__restrict__ partials, int nparts,
 }
 
 // ---------------------------------------------------------------- dequantize
-// Each lane turns 4 codes (one 4-byte load) into 4 FP32 (one 16-byte
-// non-temporal store), so every wave-wide store instruction writes 1 KiB of
-// contiguous output; a lane handles 4 such groups per work item.
+// Each lane turns 4 codes (one 4-byte load) into 4 FP32 values, written with
+// one 16-byte non-temporal store (every wave-wide store instruction writes
+// 1 KiB of contiguous output), or rounded to BF16 by gfx950's
+// v_cvt_pk_bf16_f32 (round to nearest even; checked against that rounding
+// on all 2^32 FP32 inputs) and written with one 8-byte store; a lane handles
+// 4 such groups per work item.  OUT: float or uint16_t (BF16 bits).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int FMT>
-__device__ __forceinline__ void dequant_group(uint32_t w, float s, f32x4 *dst) {
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    const __hip_bfloat162 h = __float22bfloat162_rn(make_float2(a, b));
+    uint32_t r;
+    __builtin_memcpy(&r, &h, sizeof(r));
+    return r;
+}
+
+template <int FMT, typename OUT>
+__device__ __forceinline__ void dequant_group(uint32_t w, float s, OUT *dst) {
     float v[4];
     decode4<FMT>(w, v);
     const f32x4 o = {canon(v[0] * s), canon(v[1] * s), canon(v[2] * s), canon(v[3] * s)};
-    __builtin_nontemporal_store(o, dst);
+    if constexpr (sizeof(OUT) == 4)
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(dst));
+    else
+        __builtin_nontemporal_store(u32x2{bf16x2(o.x, o.y), bf16x2(o.z, o.w)},
+                                    reinterpret_cast<u32x2 *>(dst));
 }
 
 template <int FMT>
@@ -569,17 +584,16 @@ __device__ __forceinline__ float e8m0_scale(uint32_t b) {
 // Flat walk over groups of 4 codes.  KIND: 0 per-tensor, 1 1x128 (a block is
 // 32 consecutive groups), 2 1x32 with FP32 scales (8 groups), 3 1x32 with
 // E8M0 scale bytes.
-template <int FMT, int KIND>
+template <int FMT, int KIND, typename OUT>
 __global__ __launch_bounds__(256)
 void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
-                           const void *__restrict__ scales_v, float *__restrict__ out) {
+                           const void *__restrict__ scales_v, OUT *__restrict__ out) {
     constexpr int U = 4;
     constexpr bool BLOCKED = KIND != 0;
     const float *scales = static_cast<const float *>(scales_v);
     const int64_t ngroups = n / 4;
     const float s0 = BLOCKED ? 0.0f : scales[0];
     const uint32_t *cw = reinterpret_cast<const uint32_t *>(codes);
-    f32x4 *o4 = reinterpret_cast<f32x4 *>(out);
     for (int64_t g0 = int64_t(blockIdx.x) * 256 * U; g0 < ngroups;
          g0 += int64_t(gridDim.x) * 256 * U) {
         uint32_t w[U];
@@ -596,23 +610,25 @@ void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
                 if (KIND == 1) s = scales[g >> 5];
                 if (KIND == 2) s = scales[g >> 3];
                 if (KIND == 3) s = e8m0_scale(static_cast<const uint8_t *>(scales_v)[g >> 3]);
-                dequant_group<FMT>(w[u], s, o4 + g);
+                dequant_group<FMT>(w[u], s, out + g * 4);
             }
         }
     }
     if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - ngroups * 4) {
         const int64_t i = ngroups * 4 + threadIdx.x;
-        out[i] = dequant_one<FMT>(codes[i], s0);
+        const float v = dequant_one<FMT>(codes[i], s0);
+        if constexpr (sizeof(OUT) == 4) out[i] = v;
+        else out[i] = (OUT)(bf16x2(v, 0.0f) & 0xFFFFu);
     }
 }
 
 // 128x128: a work item is a 32-row slab of one tile (4 per tile); 32 lanes
 // per 128-code row, 8 rows per pass, 4 passes.
-template <int FMT>
+template <int FMT, typename OUT>
 __global__ __launch_bounds__(256)
 void dequant_128x128_kernel(const uint8_t *__restrict__ codes, int64_t cols,
                             int64_t tiles_per_row, int64_t nitems,
-                            const float *__restrict__ scales, float *__restrict__ out) {
+                            const float *__restrict__ scales, OUT *__restrict__ out) {
     const int r_in = threadIdx.x >> 5;
     const int c4 = (threadIdx.x & 31) * 4;
     for (int64_t wi = blockIdx.x; wi < nitems; wi += gridDim.x) {
@@ -626,7 +642,7 @@ void dequant_128x128_kernel(const uint8_t *__restrict__ codes, int64_t cols,
             w[p] = *reinterpret_cast<const uint32_t *>(codes + base + int64_t(p) * 8 * cols);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            dequant_group<FMT>(w[p], s, reinterpret_cast<f32x4 *>(out + base + int64_t(p) * 8 * cols));
+            dequant_group<FMT>(w[p], s, out + base + int64_t(p) * 8 * cols);
     }
 }
 
@@ -711,28 +727,28 @@ hipError_t quantize_delayed_typed(const IN *x, int64_t rows, int64_t cols, float
     return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, typename OUT>
 hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int gran,
-                          const float *scales, float *out, hipStream_t stream) {
+                          const float *scales, OUT *out, hipStream_t stream) {
     const int64_t n = rows * cols;
     if (gran == FP8_BLOCK_128x128) {
         const int64_t tpr = cols / 128, nitems = (rows / 128) * tpr * 4;
         if (nitems == 0) return hipSuccess;
-        hipLaunchKernelGGL((dequant_128x128_kernel<FMT>), dim3(grid_for(nitems, 1)), dim3(256),
-                           0, stream, codes, cols, tpr, nitems, scales, out);
+        hipLaunchKernelGGL((dequant_128x128_kernel<FMT, OUT>), dim3(grid_for(nitems, 1)),
+                           dim3(256), 0, stream, codes, cols, tpr, nitems, scales, out);
         return hipGetLastError();
     }
     if (n == 0) return hipSuccess;
     const dim3 grid(grid_for(n / 4, 256 * 4));
     if (gran == FP8_BLOCK_1x128)
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 1>), grid, dim3(256), 0, stream, codes, n,
-                           scales, out);
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 1, OUT>), grid, dim3(256), 0, stream, codes,
+                           n, scales, out);
     else if (gran == FP8_BLOCK_1x32)
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 2>), grid, dim3(256), 0, stream, codes, n,
-                           scales, out);
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 2, OUT>), grid, dim3(256), 0, stream, codes,
+                           n, scales, out);
     else
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 0>), grid, dim3(256), 0, stream, codes, n,
-                           scales, out);
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 0, OUT>), grid, dim3(256), 0, stream, codes,
+                           n, scales, out);
     return hipGetLastError();
 }
 
@@ -740,8 +756,8 @@ template <int FMT>
 hipError_t dequantize_mx_fmt(const uint8_t *codes, int64_t n, const uint8_t *scales, float *out,
                              hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL((dequant_linear_kernel<FMT, 3>), dim3(grid_for(n / 4, 256 * 4)), dim3(256),
-                       0, stream, codes, n, scales, out);
+    hipLaunchKernelGGL((dequant_linear_kernel<FMT, 3, float>), dim3(grid_for(n / 4, 256 * 4)),
+                       dim3(256), 0, stream, codes, n, scales, out);
     return hipGetLastError();
 }
 
@@ -806,6 +822,13 @@ hipError_t launch_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols
 
 hipError_t launch_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
                              const float *scales, float *out, hipStream_t stream) {
+    if (fmt == FP8_E4M3) return dequantize_fmt<0>(codes, rows, cols, gran, scales, out, stream);
+    return dequantize_fmt<1>(codes, rows, cols, gran, scales, out, stream);
+}
+
+hipError_t launch_dequantize_bf16(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
+                                  int gran, const float *scales, uint16_t *out,
+                                  hipStream_t stream) {
     if (fmt == FP8_E4M3) return dequantize_fmt<0>(codes, rows, cols, gran, scales, out, stream);
     return dequantize_fmt<1>(codes, rows, cols, gran, scales, out, stream);
 }

@@ -288,3 +288,14 @@ def test_list_descriptors_errors():
     assert _call_descriptors([FAKE], [FAKE + 2], [10])[0] == -6
     assert _call_descriptors([FAKE], [FAKE], [-1])[0] == -2
     assert _call_descriptors([], [], [])[0] == 0
+
+
+def test_dequantize_bf16_argument_errors():
+    L = gs.lib()
+    assert L.fp8_dequantize_bf16(FAKE, 128, 100, 0, 1, FAKE, FAKE, None) == -3
+    assert L.fp8_dequantize_bf16(FAKE, 128, 128, 5, 1, FAKE, FAKE, None) == -5
+    assert L.fp8_dequantize_bf16(FAKE, 128, 128, 0, 4, FAKE, FAKE, None) == -5
+    assert L.fp8_dequantize_bf16(None, 128, 128, 0, 1, FAKE, FAKE, None) == -1
+    assert L.fp8_dequantize_bf16(FAKE, 128, 128, 0, 1, FAKE, FAKE + 8, None) == -6
+    assert L.fp8_dequantize_bf16(FAKE, -1, 128, 0, 1, FAKE, FAKE, None) == -2
+    assert L.fp8_dequantize_bf16(None, 0, 128, 0, 1, None, None, None) == 0   # empty: nothing to do
