@@ -467,26 +467,35 @@ def main():
                           dtype=torch.float32, device=dev)
         smx = torch.empty((act.rows, act.cols // 32), dtype=torch.uint8, device=dev)
         nb32, nb128 = n_a // 32, n_a // 128
-        for name, fn, nbytes in (
+        da_bf = torch.empty((act.rows, act.cols), dtype=torch.bfloat16, device=dev)
+        dw_bf = torch.empty((wgt.rows, wgt.cols), dtype=torch.bfloat16, device=dev)
+        act_wl = "%dx%d bf16 E4M3, cold (clean) infinity cache" % (act.rows, act.cols)
+        wgt_wl = "%dx%d bf16 E4M3 128x128, cold (clean) infinity cache" % (wgt.rows, wgt.cols)
+        for name, fn, nbytes, wl in (
                 ("quant_1x128_cold", lambda: gs.fp8_quantize(xa, act.fmt, act.gran, 0, ca, sa),
-                 n_a * 3 + nb128 * 4),
+                 n_a * 3 + nb128 * 4, act_wl),
                 ("dequant_1x128_cold", lambda: gs.fp8_dequantize(ca, act.fmt, act.gran, sa, da),
-                 n_a * 5 + nb128 * 4),
+                 n_a * 5 + nb128 * 4, act_wl),
+                ("dequant_1x128_bf16", lambda: gs.fp8_dequantize_bf16(ca, act.fmt, act.gran, sa,
+                                                                      da_bf),
+                 n_a * 3 + nb128 * 4, act_wl),
+                ("dequant_128x128_bf16", lambda: gs.fp8_dequantize_bf16(cw, wgt.fmt, wgt.gran, sw,
+                                                                        dw_bf),
+                 n_w * 3 + ns_w * 4, wgt_wl),
                 ("quant_1x32", lambda: gs.fp8_quantize(xa, act.fmt, gs.FP8_BLOCK_1x32, 0, ca, s32),
-                 n_a * 3 + nb32 * 4),
+                 n_a * 3 + nb32 * 4, act_wl),
                 ("dequant_1x32", lambda: gs.fp8_dequantize(ca, act.fmt, gs.FP8_BLOCK_1x32, s32, da),
-                 n_a * 5 + nb32 * 4),
-                ("quant_mx_e8m0", lambda: gs.fp8_quantize_mx(xa, act.fmt, ca, smx), n_a * 3 + nb32),
+                 n_a * 5 + nb32 * 4, act_wl),
+                ("quant_mx_e8m0", lambda: gs.fp8_quantize_mx(xa, act.fmt, ca, smx), n_a * 3 + nb32,
+                 act_wl),
                 ("dequant_mx_e8m0", lambda: gs.fp8_dequantize_mx(ca, act.fmt, smx, da),
-                 n_a * 5 + nb32)):
+                 n_a * 5 + nb32, act_wl)):
             fn()
             ms_k, _ = _time_launches(fn, 20, None if args.pmc_safe else flush)
             gbps = nbytes / (ms_k * 1e-3) / 1e9
             ext[name] = {"ms": round(ms_k, 4), "bytes": nbytes, "GBps": round(gbps, 1),
-                         "frac_of_peak": round(gbps / PEAK_GBPS, 4),
-                         "workload": "%dx%d bf16 E4M3, cold (clean) infinity cache"
-                                     % (act.rows, act.cols)}
-        del junk, junk_rd, s32, smx
+                         "frac_of_peak": round(gbps / PEAK_GBPS, 4), "workload": wl}
+        del junk, junk_rd, s32, smx, da_bf, dw_bf
 
     src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp"])
     un = kernels["unscale_check"]

@@ -38,7 +38,7 @@
 //  * The max-abs is taken on bit patterns: for non-negative floats unsigned
 //    integer order is numeric order, and BF16 halves are maxed pairwise.
 #include "device_fp8.hpp"
-#include <hip/hip_bf16.h>
+#include <type_traits>
 #include "gs_internal.hpp"
 
 // Cache policy per kernel (1 = non-temporal), chosen by measurement.
@@ -541,31 +541,52 @@ void delayed_update_kernel(const uint32_t *__restrict__ partials, int nparts,
 }
 
 // ---------------------------------------------------------------- dequantize
-// Each lane turns 4 codes (one 4-byte load) into 4 FP32 values, written with
-// one 16-byte non-temporal store (every wave-wide store instruction writes
-// 1 KiB of contiguous output), or rounded to BF16 by gfx950's
-// v_cvt_pk_bf16_f32 (round to nearest even; checked against that rounding
-// on all 2^32 FP32 inputs) and written with one 8-byte store; a lane handles
-// 4 such groups per work item.  OUT: float or uint16_t (BF16 bits).
+// A lane turns a group of codes into one 16-byte non-temporal store, so
+// every wave-wide store instruction writes 1 KiB of contiguous output: 4
+// codes (one 4-byte load) into 4 FP32 values, or 8 codes (one 8-byte load)
+// into 8 BF16 values, rounded by gfx950's v_cvt_pk_bf16_f32 (round to
+// nearest even; checked against that rounding on all 2^32 FP32 inputs).
+// OUT: float or uint16_t (BF16 bits).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+template <typename OUT>
+struct DqGroup {
+    static constexpr int kCodes = sizeof(OUT) == 4 ? 4 : 8;    // codes per lane per group
+    // groups per lane per work item of the flat walk (BF16: 2, measured
+    // back to back 1.3% ahead of 4 on 16384x7168 codes)
+    static constexpr int kUnroll = sizeof(OUT) == 4 ? 4 : 2;
+    typedef typename std::conditional<kCodes == 4, uint32_t, u32x2>::type Word;
+};
+
+// Two FP32 values rounded to BF16 (a in the low half): one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
-    const __hip_bfloat162 h = __float22bfloat162_rn(make_float2(a, b));
+    const bf16x2_t h = __builtin_convertvector(f32x2{a, b}, bf16x2_t);
     uint32_t r;
     __builtin_memcpy(&r, &h, sizeof(r));
     return r;
 }
 
-template <int FMT, typename OUT>
-__device__ __forceinline__ void dequant_group(uint32_t w, float s, OUT *dst) {
+template <int FMT>
+__device__ __forceinline__ void dequant_group(uint32_t w, float s, float *dst) {
     float v[4];
     decode4<FMT>(w, v);
     const f32x4 o = {canon(v[0] * s), canon(v[1] * s), canon(v[2] * s), canon(v[3] * s)};
-    if constexpr (sizeof(OUT) == 4)
-        __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(dst));
-    else
-        __builtin_nontemporal_store(u32x2{bf16x2(o.x, o.y), bf16x2(o.z, o.w)},
-                                    reinterpret_cast<u32x2 *>(dst));
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(dst));
+}
+
+template <int FMT>
+__device__ __forceinline__ void dequant_group(u32x2 w, float s, uint16_t *dst) {
+    float v[8];
+    decode4<FMT>(w.x, *reinterpret_cast<float(*)[4]>(v));
+    decode4<FMT>(w.y, *reinterpret_cast<float(*)[4]>(v + 4));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = canon(v[k] * s);
+    __builtin_nontemporal_store(u32x4{bf16x2(v[0], v[1]), bf16x2(v[2], v[3]),
+                                      bf16x2(v[4], v[5]), bf16x2(v[6], v[7])},
+                                reinterpret_cast<u32x4 *>(dst));
 }
 
 template <int FMT>
@@ -581,68 +602,77 @@ __device__ __forceinline__ float e8m0_scale(uint32_t b) {
     return b == 0xFFu ? as_f32(0x7FC00000u) : as_f32(b ? (b << 23) : 0x00400000u);
 }
 
-// Flat walk over groups of 4 codes.  KIND: 0 per-tensor, 1 1x128 (a block is
-// 32 consecutive groups), 2 1x32 with FP32 scales (8 groups), 3 1x32 with
-// E8M0 scale bytes.
+// Flat walk over groups of 4 codes (FP32 output) or 8 (BF16).  KIND: 0
+// per-tensor, 1 1x128, 2 1x32 with FP32 scales, 3 1x32 with E8M0 scale
+// bytes; a block holds a whole number of groups.
 template <int FMT, int KIND, typename OUT>
 __global__ __launch_bounds__(256)
 void dequant_linear_kernel(const uint8_t *__restrict__ codes, int64_t n,
                            const void *__restrict__ scales_v, OUT *__restrict__ out) {
-    constexpr int U = 4;
+    constexpr int U = DqGroup<OUT>::kUnroll;
     constexpr bool BLOCKED = KIND != 0;
+    constexpr int kCodes = DqGroup<OUT>::kCodes;
+    constexpr int kShift = kCodes == 4 ? 2 : 3;                // log2(codes per group)
+    typedef typename DqGroup<OUT>::Word Word;
     const float *scales = static_cast<const float *>(scales_v);
-    const int64_t ngroups = n / 4;
+    const int64_t ngroups = n / kCodes;
     const float s0 = BLOCKED ? 0.0f : scales[0];
-    const uint32_t *cw = reinterpret_cast<const uint32_t *>(codes);
+    const Word *cw = reinterpret_cast<const Word *>(codes);
     for (int64_t g0 = int64_t(blockIdx.x) * 256 * U; g0 < ngroups;
          g0 += int64_t(gridDim.x) * 256 * U) {
-        uint32_t w[U];
+        Word w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + u * 256 + threadIdx.x;
-            w[u] = g < ngroups ? cw[g] : 0u;
+            w[u] = g < ngroups ? cw[g] : Word{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + u * 256 + threadIdx.x;
             if (g < ngroups) {
                 float s = s0;
-                if (KIND == 1) s = scales[g >> 5];
-                if (KIND == 2) s = scales[g >> 3];
-                if (KIND == 3) s = e8m0_scale(static_cast<const uint8_t *>(scales_v)[g >> 3]);
-                dequant_group<FMT>(w[u], s, out + g * 4);
+                if (KIND == 1) s = scales[g >> (7 - kShift)];
+                if (KIND == 2) s = scales[g >> (5 - kShift)];
+                if (KIND == 3) s = e8m0_scale(static_cast<const uint8_t *>(scales_v)[g >> (5 - kShift)]);
+                dequant_group<FMT>(w[u], s, out + g * kCodes);
             }
         }
     }
-    if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - ngroups * 4) {
-        const int64_t i = ngroups * 4 + threadIdx.x;
+    if (!BLOCKED && blockIdx.x == 0 && threadIdx.x < n - ngroups * kCodes) {
+        const int64_t i = ngroups * kCodes + threadIdx.x;
         const float v = dequant_one<FMT>(codes[i], s0);
         if constexpr (sizeof(OUT) == 4) out[i] = v;
         else out[i] = (OUT)(bf16x2(v, 0.0f) & 0xFFFFu);
     }
 }
 
-// 128x128: a work item is a 32-row slab of one tile (4 per tile); 32 lanes
-// per 128-code row, 8 rows per pass, 4 passes.
+// 128x128: a work item is a 32-row slab of one tile (4 per tile).  FP32
+// output: 32 lanes per 128-code row, 8 rows per pass, 4 passes; BF16: 16
+// lanes per row, 16 rows per pass, 2 passes.
 template <int FMT, typename OUT>
 __global__ __launch_bounds__(256)
 void dequant_128x128_kernel(const uint8_t *__restrict__ codes, int64_t cols,
                             int64_t tiles_per_row, int64_t nitems,
                             const float *__restrict__ scales, OUT *__restrict__ out) {
-    const int r_in = threadIdx.x >> 5;
-    const int c4 = (threadIdx.x & 31) * 4;
+    constexpr int kCodes = DqGroup<OUT>::kCodes;
+    constexpr int kLanesPerRow = 128 / kCodes;
+    constexpr int kRowsPerPass = 256 / kLanesPerRow;
+    constexpr int kPasses = 32 / kRowsPerPass;
+    typedef typename DqGroup<OUT>::Word Word;
+    const int r_in = threadIdx.x / kLanesPerRow;
+    const int c0 = (threadIdx.x % kLanesPerRow) * kCodes;
     for (int64_t wi = blockIdx.x; wi < nitems; wi += gridDim.x) {
         const int64_t t = wi >> 2, slab = wi & 3;
         const int64_t ti = t / tiles_per_row, tj = t - ti * tiles_per_row;
         const float s = scales[t];
-        const int64_t base = (ti * 128 + slab * 32 + r_in) * cols + tj * 128 + c4;
-        uint32_t w[4];
+        const int64_t base = (ti * 128 + slab * 32 + r_in) * cols + tj * 128 + c0;
+        Word w[kPasses];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            w[p] = *reinterpret_cast<const uint32_t *>(codes + base + int64_t(p) * 8 * cols);
+        for (int p = 0; p < kPasses; ++p)
+            w[p] = *reinterpret_cast<const Word *>(codes + base + int64_t(p) * kRowsPerPass * cols);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            dequant_group<FMT>(w[p], s, out + base + int64_t(p) * 8 * cols);
+        for (int p = 0; p < kPasses; ++p)
+            dequant_group<FMT>(w[p], s, out + base + int64_t(p) * kRowsPerPass * cols);
     }
 }
 
@@ -739,7 +769,7 @@ hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int 
         return hipGetLastError();
     }
     if (n == 0) return hipSuccess;
-    const dim3 grid(grid_for(n / 4, 256 * 4));
+    const dim3 grid(grid_for(n / DqGroup<OUT>::kCodes, 256 * DqGroup<OUT>::kUnroll));
     if (gran == FP8_BLOCK_1x128)
         hipLaunchKernelGGL((dequant_linear_kernel<FMT, 1, OUT>), grid, dim3(256), 0, stream, codes,
                            n, scales, out);

@@ -38,6 +38,8 @@ int orc_quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, i
                          uint8_t *codes, float *scale_used, int32_t *nonfinite);
 int orc_dequantize(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
                    const float *scales, float *out);
+int orc_dequantize_bf16(const uint8_t *codes, int64_t rows, int64_t cols, int fmt, int gran,
+                        const float *scales, uint16_t *out);
 int orc_quantize_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
                     uint8_t *codes, uint8_t *scales_e8m0, int32_t *nonfinite);
 int orc_dequantize_mx(const uint8_t *codes, int64_t rows, int64_t cols, int fmt,
@@ -191,6 +193,16 @@ static void test_quantize(void) {
                     expect(orc_quantize(x, dtype, r, c, fmt, gran, mode, codes, sc, &nf) == 0,
                            "quantize returns 0");
                     expect(orc_dequantize(codes, r, c, fmt, gran, sc, out) == 0, "dequantize returns 0");
+                    uint16_t *out16 = (uint16_t *)xmalloc((size_t)n * 2);
+                    expect(orc_dequantize_bf16(codes, r, c, fmt, gran, sc, out16) == 0,
+                           "bf16 dequantize returns 0");
+                    for (int64_t i = 0; i < n; ++i) {
+                        uint32_t b;
+                        memcpy(&b, &out[i], 4);
+                        if (isnan(out[i])) expect(out16[i] == 0x7FC0u, "bf16 NaN is canonical");
+                        else if ((b & 0xFFFFu) == 0) expect(out16[i] == (uint16_t)(b >> 16), "exact bf16 kept");
+                    }
+                    free(out16);
                     if (gran == 3 && mode == 0) {
                         uint8_t *e8 = (uint8_t *)xmalloc((size_t)ns);
                         expect(orc_quantize_mx(x, dtype, r, c, fmt, codes, e8, &nf) == 0, "mx quantize");
