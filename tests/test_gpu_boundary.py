@@ -1,8 +1,9 @@
 """GPU checks of the boundary's own machinery, through the C ABI against the
 oracle: the device cache of gradient-list descriptors under eviction, calls
-from several host threads on their own streams, and a whole step captured in
-a HIP graph (after the list's first call, the library allocates nothing and
-records no memset), replayed with eager work between the replays."""
+from several host threads on their own streams, and whole steps captured in
+HIP graphs (after the list's first call, the library allocates nothing and
+records no memset) -- the core step, and one that calls every other entry
+point -- replayed with eager work between the replays."""
 import threading
 
 import numpy as np
@@ -176,3 +177,133 @@ def test_step_captured_in_a_hip_graph(dev):
             grads[inj_t][inj_i:inj_i + 1] = _to_dev(np.array([orig], np.uint16), dev)
     # closed form: replays 1-2 clean, 3 skipped (S halves), 4-6 clean (tracker 3 < 4)
     assert (float(R.S), R.skips.value, R.tracker.value) == (g.scale / 2, 1, 3)
+
+
+def _bf16_bits(x):
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_extended_step_captured_in_a_hip_graph(dev):
+    """The other entry points captured once and replayed 6 times: unscale with
+    the exact sum of squares, the hysteresis update (Infs before replays 3
+    and 4 spend the budget, then lower S), a delayed-scaling step, a
+    per-tensor E5M2 quantize with its BF16 dequantize, a 128x128 quantize
+    with its BF16 dequantize, and an MX quantize + dequantize.  The input
+    matrix is rewritten eagerly between replays (a new magnitude each time),
+    so the delayed history moves; every replay matches the oracle."""
+    rng = np.random.default_rng(77)
+    sizes = (3000, 20000, 517)
+    host = [_random_f16(rng, n) & np.uint16(0xBBFF) for n in sizes]   # finite, |g| < 1
+    grads = [_to_dev(h, dev) for h in host]
+    outs = [torch.empty(n, dtype=torch.float32, device=dev) for n in sizes]
+    R, C = 256, 512
+    xs = [_bf16_bits(rng.standard_normal((R, C)).astype(np.float32) * np.float32(2.0 ** (r % 3 - 1)))
+          for r in range(7)]
+    x = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    ws_sq = torch.empty(gs.gs_unscale_check_sumsq_workspace_size(list(sizes)), dtype=torch.uint8, device=dev)
+    ws_pt = torch.empty(gs.fp8_quantize_workspace_size(R, C, gs.FP8_PER_TENSOR), dtype=torch.uint8, device=dev)
+    ws_dl = torch.empty(gs.fp8_quantize_workspace_size(R, C, gs.FP8_PER_TENSOR), dtype=torch.uint8, device=dev)
+    S = torch.empty(1, dtype=torch.float32, device=dev)
+    tr = torch.empty(1, dtype=torch.int32, device=dev)
+    h = torch.empty(1, dtype=torch.int32, device=dev)
+    found = torch.empty(1, dtype=torch.int32, device=dev)
+    skips = torch.empty(1, dtype=torch.int64, device=dev)
+    acc = torch.empty(2, dtype=torch.int64, device=dev)
+    nsq = torch.empty(1, dtype=torch.float64, device=dev)
+    st = torch.empty(1, dtype=torch.float32, device=dev)
+    hist = torch.empty(4, dtype=torch.float32, device=dev)
+    pos = torch.empty(1, dtype=torch.int32, device=dev)
+    c_dl = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    used = torch.empty(1, dtype=torch.float32, device=dev)
+    c_pt = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    s_pt = torch.empty(1, dtype=torch.float32, device=dev)
+    d_pt = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    c_tl = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    s_tl = torch.empty(gs.scale_shape(R, C, gs.FP8_BLOCK_128x128), dtype=torch.float32, device=dev)
+    d_tl = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    c_mx = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    s_mx = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+    d_mx = torch.empty((R, C), dtype=torch.float32, device=dev)
+
+    def reset():
+        S.fill_(65536.0)
+        tr.zero_()
+        h.fill_(2)
+        found.zero_()
+        skips.zero_()
+        st.fill_(1.0)
+        hist.zero_()
+        pos.zero_()
+
+    def step():
+        gs.gs_unscale_check_sumsq(grads, outs, S, found, acc, nsq, ws_sq)
+        gs.gs_update_scale_hysteresis(S, tr, h, found, 2.0, 0.5, 3, 2, False, 1.0, skips)
+        gs.fp8_quantize_delayed(x, gs.FP8_E4M3, st, hist, pos, c_dl, used, None, ws_dl)
+        gs.fp8_quantize(x, gs.FP8_E5M2, gs.FP8_PER_TENSOR, gs.FP8_SCALE_FROM_AMAX, c_pt, s_pt, None, ws_pt)
+        gs.fp8_dequantize_bf16(c_pt, gs.FP8_E5M2, gs.FP8_PER_TENSOR, s_pt, d_pt)
+        gs.fp8_quantize(x, gs.FP8_E4M3, gs.FP8_BLOCK_128x128, gs.FP8_SCALE_FROM_AMAX, c_tl, s_tl)
+        gs.fp8_dequantize_bf16(c_tl, gs.FP8_E4M3, gs.FP8_BLOCK_128x128, s_tl, d_tl)
+        gs.fp8_quantize_mx(x, gs.FP8_E4M3, c_mx, s_mx)
+        gs.fp8_dequantize_mx(c_mx, gs.FP8_E4M3, s_mx, d_mx)
+
+    x.copy_(torch.from_numpy(xs[0].view(np.int16)).view(torch.bfloat16))
+    reset()
+    acc.zero_()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # caches the descriptors, warms up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    RS = oracle.HysteresisState(65536.0, 0, 2)
+    RD = oracle.DelayedState(4, 1.0)
+    inj_t, inj_i = 1, 4321
+    for r in range(1, 7):
+        bad = r in (3, 4)
+        host[inj_t][inj_i] = 0x7C00 if bad else 0x3C00
+        grads[inj_t][inj_i:inj_i + 1] = _to_dev(np.array([host[inj_t][inj_i]], np.uint16), dev)
+        x.copy_(torch.from_numpy(xs[r].view(np.int16)).view(torch.bfloat16))
+        acc.zero_()                              # the caller zeroes the running total per step
+        for o in outs:
+            o.fill_(-2.0)
+        for t in (c_dl, c_pt, c_tl, c_mx, s_mx):
+            t.zero_()
+        for t in (d_pt, d_tl, d_mx):
+            t.zero_()
+        graph.replay()
+        ref, rf, racc, rnsq = oracle.unscale_check_sumsq(host, float(RS.S))
+        RS.found_inf.value = rf
+        oracle.update_scale_hysteresis(RS, 2.0, 0.5, 3, 2, False, 1.0)
+        rc_dl, ru, _ = oracle.quantize_delayed(xs[r], gs.FP8_E4M3, RD)
+        rc_pt, rs_pt, _ = oracle.quantize(xs[r], gs.FP8_E5M2, gs.FP8_PER_TENSOR)
+        rc_tl, rs_tl, _ = oracle.quantize(xs[r], gs.FP8_E4M3, gs.FP8_BLOCK_128x128)
+        rc_mx, rs_mx, _ = oracle.quantize_mx(xs[r], gs.FP8_E4M3)
+        torch.cuda.synchronize()
+        for o, rr in zip(outs, ref):
+            assert np.array_equal(_bits(o), rr.view(np.uint32)), r
+        assert tuple(int(v) & ((1 << 64) - 1) for v in acc.cpu().tolist()) == tuple(racc), r
+        assert float(nsq.item()) == rnsq, r
+        assert (float(S.item()), int(tr.item()), int(h.item()), int(skips.item()), int(found.item())) == \
+            (float(RS.S), RS.tracker.value, RS.h.value, RS.skips.value, 0), r
+        assert np.array_equal(c_dl.cpu().numpy(), rc_dl), r
+        assert np.float32(used.item()).view(np.uint32) == np.float32(ru).view(np.uint32), r
+        assert np.array_equal(hist.cpu().numpy().view(np.uint32), RD.history.view(np.uint32)), r
+        assert np.float32(st.item()).view(np.uint32) == RD.scale.view(np.uint32)[0], r
+        assert np.array_equal(c_pt.cpu().numpy(), rc_pt), r
+        assert np.array_equal(s_pt.cpu().numpy().view(np.uint32), rs_pt.reshape(-1).view(np.uint32)), r
+        assert np.array_equal(d_pt.view(torch.int16).cpu().numpy().view(np.uint16),
+                              oracle.dequantize_bf16(rc_pt, gs.FP8_E5M2, gs.FP8_PER_TENSOR, rs_pt)), r
+        assert np.array_equal(c_tl.cpu().numpy(), rc_tl), r
+        assert np.array_equal(s_tl.cpu().numpy().reshape(-1).view(np.uint32), rs_tl.reshape(-1).view(np.uint32)), r
+        assert np.array_equal(d_tl.view(torch.int16).cpu().numpy().view(np.uint16),
+                              oracle.dequantize_bf16(rc_tl, gs.FP8_E4M3, gs.FP8_BLOCK_128x128, rs_tl)), r
+        assert np.array_equal(c_mx.cpu().numpy(), rc_mx) and np.array_equal(s_mx.cpu().numpy(), rs_mx), r
+        assert np.array_equal(_bits(d_mx), oracle.dequantize_mx(rc_mx, gs.FP8_E4M3, rs_mx).view(np.uint32)), r
+    # closed form: replays 1-2 clean (tracker 2), 3 spends the budget, 4 lowers S, 5-6 clean
+    assert (float(RS.S), RS.skips.value, RS.tracker.value) == (32768.0, 2, 2)
