@@ -91,15 +91,78 @@ def _check(status: int, where: str) -> None:
         raise GSError(status, where)
 
 
-def _stream(stream) -> int | None:
+def _gpu(t, name: str, dtypes, dev=None, numel: int | None = None, exact: bool = False,
+         optional: bool = False):
+    """Checks that t is a contiguous GPU tensor of one of `dtypes`, on `dev`
+    when given, holding at least (or, with exact, exactly) `numel` elements;
+    returns its device.  The C ABI takes bare device pointers and cannot see
+    any of this: a host tensor or a short buffer would reach a kernel."""
+    import torch
+    if t is None:
+        if optional:
+            return dev
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU, not on %s" % (name, t.device))
+    if dev is not None and t.device != dev:
+        raise ValueError("%s is on %s, the other arguments on %s" % (name, t.device, dev))
+    if t.dtype not in dtypes:
+        raise TypeError("%s must be %s, not %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if numel is not None and (t.numel() != numel if exact else t.numel() < numel):
+        raise ValueError("%s holds %d elements, %s%d needed" %
+                         (name, t.numel(), "" if exact else "at least ", numel))
+    return t.device
+
+
+def _bytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream, dev) -> int | None:
+    """The HIP stream handle: torch's current stream on dev by default; a
+    torch stream must belong to dev; an integer is passed as is."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        return torch.cuda.current_stream(dev).cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        if stream.device != dev:
+            raise ValueError("the stream is on %s, the tensors on %s" % (stream.device, dev))
+        return stream.cuda_stream
+    return stream
+
+
+def _call(dev, where: str, fn, *args) -> None:
+    """Calls a C entry point with the tensors' device current (the unscale's
+    descriptor cache allocates on the current device) and raises on error."""
+    import torch
+    with torch.cuda.device(dev):
+        status = fn(*args)
+    _check(status, where)
 
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def _input_dtype(x) -> int:
+    import torch
+    if x.dtype == torch.bfloat16:
+        return GS_BF16
+    if x.dtype == torch.float32:
+        return GS_F32
+    raise TypeError("x must be bfloat16 or float32, not %s" % x.dtype)
+
+
+def _matrix(x, name: str, dtypes):
+    """A contiguous 2-D GPU tensor: returns (rows, cols, device)."""
+    dev = _gpu(x, name, dtypes)
+    if x.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    return x.shape[0], x.shape[1], dev
 
 
 def n_scales(rows: int, cols: int, gran: int) -> int:
@@ -123,22 +186,36 @@ def scale_shape(rows: int, cols: int, gran: int) -> tuple:
 
 
 # ------------------------------------------------------------------ unscale
+def _scalars(dev, **kw):
+    """The device-resident scalars of the scaler state: name -> (tensor,
+    dtypes, elements needed, optional)."""
+    for name, (t, dtypes, k, opt) in kw.items():
+        _gpu(t, name, dtypes, dev, k, optional=opt)
+
+
 def gs_unscale_check(grads: Sequence, outs: Sequence, scale, found_inf, stream=None) -> None:
     """FP16 gradients -> FP32 outputs multiplied by fl32(1/S); found_inf set to
     1 on any non-finite output.  One kernel launch for the whole list."""
-    n, arr_g, arr_o, arr_n = _grad_lists(grads, outs)
-    _check(lib().gs_unscale_check(n, arr_g, arr_o, arr_n, GS_F16, _ptr(scale), _ptr(found_inf),
-                                  _stream(stream)), "gs_unscale_check")
+    import torch
+    dev = _gpu(scale, "scale", (torch.float32,), None, 1)
+    _gpu(found_inf, "found_inf", (torch.int32,), dev, 1)
+    n, arr_g, arr_o, arr_n = _grad_lists(grads, outs, dev)
+    _call(dev, "gs_unscale_check", lib().gs_unscale_check, n, arr_g, arr_o, arr_n, GS_F16,
+          _ptr(scale), _ptr(found_inf), _stream(stream, dev))
 
 
-def _grad_lists(grads, outs):
+def _grad_lists(grads, outs, dev):
     import torch
     n = len(grads)
     if len(outs) != n:
         raise ValueError("grads and outs differ in length")
     for g, o in zip(grads, outs):
+        if not isinstance(g, torch.Tensor) or not isinstance(o, torch.Tensor):
+            raise TypeError("grads and outs must be torch tensors")
         if g.dtype != torch.float16 or o.dtype != torch.float32:
             raise TypeError("grads must be float16 and outs float32")
+        if g.device != dev or o.device != dev:
+            raise ValueError("every gradient and output must be on %s (the scale's device)" % dev)
         if o.numel() != g.numel() or not g.is_contiguous() or not o.is_contiguous():
             raise ValueError("each out must be a contiguous float32 tensor of its grad's size")
     arr_g = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
@@ -159,28 +236,32 @@ def gs_unscale_check_sumsq(grads: Sequence, outs: Sequence, scale, found_inf, su
     gradients, added to sumsq (int64 [2], low and high words), and the
     recovered-gradient norm squared written to norm_sq (float64 [1])."""
     import torch
-    n, arr_g, arr_o, arr_n = _grad_lists(grads, outs)
-    if sumsq.dtype not in (torch.int64, torch.uint64) or sumsq.numel() != 2:
-        raise TypeError("sumsq must be a 2-element int64 tensor")
-    if norm_sq.dtype != torch.float64:
-        raise TypeError("norm_sq must be float64")
+    dev = _gpu(scale, "scale", (torch.float32,), None, 1)
+    _gpu(found_inf, "found_inf", (torch.int32,), dev, 1)
+    _gpu(sumsq, "sumsq", (torch.int64, torch.uint64), dev, 2, exact=True)
+    _gpu(norm_sq, "norm_sq", (torch.float64,), dev, 1)
+    n, arr_g, arr_o, arr_n = _grad_lists(grads, outs, dev)
     ws_bytes = gs_unscale_check_sumsq_workspace_size([g.numel() for g in grads])
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scale.device)
-    _check(lib().gs_unscale_check_sumsq(n, arr_g, arr_o, arr_n, GS_F16, _ptr(scale),
-                                        _ptr(found_inf), _ptr(sumsq), _ptr(norm_sq),
-                                        _ptr(workspace), workspace.numel(), _stream(stream)),
-           "gs_unscale_check_sumsq")
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _gpu(workspace, "workspace", (torch.uint8,), dev, ws_bytes)
+    _call(dev, "gs_unscale_check_sumsq", lib().gs_unscale_check_sumsq, n, arr_g, arr_o, arr_n,
+          GS_F16, _ptr(scale), _ptr(found_inf), _ptr(sumsq), _ptr(norm_sq), _ptr(workspace),
+          _bytes(workspace), _stream(stream, dev))
 
 
 def gs_update_scale(scale, growth_tracker, found_inf, growth_factor: float = 2.0,
                     backoff_factor: float = 0.5, growth_interval: int = 2000,
                     skip_count=None, stream=None) -> None:
     """Grow/backoff/skip update of the device-resident loss scale."""
-    _check(lib().gs_update_scale(_ptr(scale), _ptr(growth_tracker), _ptr(found_inf),
-                                 float(growth_factor), float(backoff_factor),
-                                 int(growth_interval), _ptr(skip_count), _stream(stream)),
-           "gs_update_scale")
+    import torch
+    dev = _gpu(scale, "scale", (torch.float32,), None, 1)
+    _scalars(dev, growth_tracker=(growth_tracker, (torch.int32,), 1, False),
+             found_inf=(found_inf, (torch.int32,), 1, False),
+             skip_count=(skip_count, (torch.int64,), 1, True))
+    _call(dev, "gs_update_scale", lib().gs_update_scale, _ptr(scale), _ptr(growth_tracker),
+          _ptr(found_inf), float(growth_factor), float(backoff_factor), int(growth_interval),
+          _ptr(skip_count), _stream(stream, dev))
 
 
 def gs_update_scale_hysteresis(scale, growth_tracker, hysteresis_left, found_inf,
@@ -190,11 +271,17 @@ def gs_update_scale_hysteresis(scale, growth_tracker, hysteresis_left, found_inf
                                skip_count=None, stream=None) -> None:
     """Update with a hysteresis budget, a floor and a growth window (defaults:
     the DeepSpeed fp16 block's 1000 / 2 / false / 1)."""
-    _check(lib().gs_update_scale_hysteresis(
-        _ptr(scale), _ptr(growth_tracker), _ptr(hysteresis_left), _ptr(found_inf),
-        float(growth_factor), float(backoff_factor), int(growth_interval), int(hysteresis),
-        int(bool(consecutive_hysteresis)), float(min_scale), _ptr(skip_count),
-        _stream(stream)), "gs_update_scale_hysteresis")
+    import torch
+    dev = _gpu(scale, "scale", (torch.float32,), None, 1)
+    _scalars(dev, growth_tracker=(growth_tracker, (torch.int32,), 1, False),
+             hysteresis_left=(hysteresis_left, (torch.int32,), 1, False),
+             found_inf=(found_inf, (torch.int32,), 1, False),
+             skip_count=(skip_count, (torch.int64,), 1, True))
+    _call(dev, "gs_update_scale_hysteresis", lib().gs_update_scale_hysteresis, _ptr(scale),
+          _ptr(growth_tracker), _ptr(hysteresis_left), _ptr(found_inf), float(growth_factor),
+          float(backoff_factor), int(growth_interval), int(hysteresis),
+          int(bool(consecutive_hysteresis)), float(min_scale), _ptr(skip_count),
+          _stream(stream, dev))
 
 
 # ------------------------------------------------------------------ FP8
@@ -208,30 +295,24 @@ def fp8_quantize(x, fmt: int, gran: int, mode: int = FP8_SCALE_FROM_AMAX, codes=
     codes is uint8 [rows, cols]; scales float32 in the block layout.  In
     given-scale mode `scales` must be supplied."""
     import torch
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
-    rows, cols = x.shape
-    if x.dtype == torch.bfloat16:
-        dt = GS_BF16
-    elif x.dtype == torch.float32:
-        dt = GS_F32
-    else:
-        raise TypeError("x must be bfloat16 or float32")
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    rows, cols, dev = _matrix(x, "x", (torch.bfloat16, torch.float32))
+    dt = _input_dtype(x)
     if codes is None:
-        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scales is None:
         if mode == FP8_SCALE_GIVEN:
             raise ValueError("given-scale mode needs scales")
-        scales = torch.empty(scale_shape(rows, cols, gran), dtype=torch.float32, device=x.device)
+        scales = torch.empty(scale_shape(rows, cols, gran), dtype=torch.float32, device=dev)
+    _gpu(codes, "codes", (torch.uint8,), dev, rows * cols, exact=True)
+    _gpu(scales, "scales", (torch.float32,), dev, n_scales(rows, cols, gran))
+    _gpu(nonfinite, "nonfinite", (torch.int32,), dev, 1, optional=True)
     ws_bytes = fp8_quantize_workspace_size(rows, cols, gran)
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    _check(lib().fp8_quantize(_ptr(x), dt, rows, cols, int(fmt), int(gran), int(mode),
-                              _ptr(codes), _ptr(scales), _ptr(nonfinite), _ptr(workspace),
-                              ws_bytes if workspace is not None else 0, _stream(stream)),
-           "fp8_quantize")
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _gpu(workspace, "workspace", (torch.uint8,), dev, ws_bytes, optional=True)
+    _call(dev, "fp8_quantize", lib().fp8_quantize, _ptr(x), dt, rows, cols, int(fmt), int(gran),
+          int(mode), _ptr(codes), _ptr(scales), _ptr(nonfinite), _ptr(workspace),
+          _bytes(workspace), _stream(stream, dev))
     return codes, scales
 
 
@@ -241,52 +322,53 @@ def fp8_quantize_delayed(x, fmt: int, scale_state, amax_history, history_pos, co
     with the scale in scale_state, record this step's amax in the history
     ring, write the next step's scale.  Returns (codes, scale_used)."""
     import torch
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
-    rows, cols = x.shape
-    dt = GS_BF16 if x.dtype == torch.bfloat16 else GS_F32 if x.dtype == torch.float32 else None
-    if dt is None:
-        raise TypeError("x must be bfloat16 or float32")
+    rows, cols, dev = _matrix(x, "x", (torch.bfloat16, torch.float32))
+    dt = _input_dtype(x)
+    _gpu(scale_state, "scale_state", (torch.float32,), dev, 1)
+    _gpu(amax_history, "amax_history", (torch.float32,), dev)
+    _gpu(history_pos, "history_pos", (torch.int32,), dev, 1)
     if codes is None:
-        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scale_used is None:
-        scale_used = torch.empty(1, dtype=torch.float32, device=x.device)
+        scale_used = torch.empty(1, dtype=torch.float32, device=dev)
+    _gpu(codes, "codes", (torch.uint8,), dev, rows * cols, exact=True)
+    _gpu(scale_used, "scale_used", (torch.float32,), dev, 1)
+    _gpu(nonfinite, "nonfinite", (torch.int32,), dev, 1, optional=True)
     ws_bytes = fp8_quantize_workspace_size(rows, cols, FP8_PER_TENSOR)
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    _check(lib().fp8_quantize_delayed(_ptr(x), dt, rows, cols, int(fmt), _ptr(scale_state),
-                                      _ptr(amax_history), amax_history.numel(),
-                                      _ptr(history_pos), _ptr(codes), _ptr(scale_used),
-                                      _ptr(nonfinite), _ptr(workspace), ws_bytes,
-                                      _stream(stream)), "fp8_quantize_delayed")
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _gpu(workspace, "workspace", (torch.uint8,), dev, ws_bytes)
+    _call(dev, "fp8_quantize_delayed", lib().fp8_quantize_delayed, _ptr(x), dt, rows, cols,
+          int(fmt), _ptr(scale_state), _ptr(amax_history), amax_history.numel(),
+          _ptr(history_pos), _ptr(codes), _ptr(scale_used), _ptr(nonfinite), _ptr(workspace),
+          _bytes(workspace), _stream(stream, dev))
     return codes, scale_used
+
+
+def _dequantize(entry, out_dtype, codes, fmt, gran, scales, out, stream):
+    import torch
+    rows, cols, dev = _matrix(codes, "codes", (torch.uint8,))
+    _gpu(scales, "scales", (torch.float32,), dev, n_scales(rows, cols, gran))
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    _gpu(out, "out", (out_dtype,), dev, rows * cols, exact=True)
+    _call(dev, entry, getattr(lib(), entry), _ptr(codes), rows, cols, int(fmt), int(gran),
+          _ptr(scales), _ptr(out), _stream(stream, dev))
+    return out
 
 
 def fp8_dequantize(codes, fmt: int, gran: int, scales, out=None, stream=None):
     """decode(code) * s in float32; returns out [rows, cols]."""
     import torch
-    if codes.dim() != 2 or codes.dtype != torch.uint8:
-        raise TypeError("codes must be a 2-D uint8 tensor")
-    rows, cols = codes.shape
-    if out is None:
-        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
-    _check(lib().fp8_dequantize(_ptr(codes), rows, cols, int(fmt), int(gran), _ptr(scales),
-                                _ptr(out), _stream(stream)), "fp8_dequantize")
-    return out
+    return _dequantize("fp8_dequantize", torch.float32, codes, fmt, gran, scales, out, stream)
 
 
 def fp8_dequantize_bf16(codes, fmt: int, gran: int, scales, out=None, stream=None):
     """decode(code) * s in float32, rounded to bfloat16 (nearest, ties to
     even); returns out [rows, cols] (torch.bfloat16)."""
     import torch
-    if codes.dim() != 2 or codes.dtype != torch.uint8:
-        raise TypeError("codes must be a 2-D uint8 tensor")
-    rows, cols = codes.shape
-    if out is None:
-        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
-    _check(lib().fp8_dequantize_bf16(_ptr(codes), rows, cols, int(fmt), int(gran), _ptr(scales),
-                                     _ptr(out), _stream(stream)), "fp8_dequantize_bf16")
-    return out
+    return _dequantize("fp8_dequantize_bf16", torch.bfloat16, codes, fmt, gran, scales, out,
+                       stream)
 
 
 def fp8_quantize_mx(x, fmt: int, codes=None, scales=None, nonfinite=None, stream=None):
@@ -294,29 +376,28 @@ def fp8_quantize_mx(x, fmt: int, codes=None, scales=None, nonfinite=None, stream
     bfloat16/float32 CUDA tensor; returns (codes uint8 [rows, cols], scales
     uint8 [rows, cols/32])."""
     import torch
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
-    rows, cols = x.shape
-    dt = GS_BF16 if x.dtype == torch.bfloat16 else GS_F32 if x.dtype == torch.float32 else None
-    if dt is None:
-        raise TypeError("x must be bfloat16 or float32")
+    rows, cols, dev = _matrix(x, "x", (torch.bfloat16, torch.float32))
+    dt = _input_dtype(x)
     if codes is None:
-        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
-    _check(lib().fp8_quantize_mx(_ptr(x), dt, rows, cols, int(fmt), _ptr(codes), _ptr(scales),
-                                 _ptr(nonfinite), _stream(stream)), "fp8_quantize_mx")
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    _gpu(codes, "codes", (torch.uint8,), dev, rows * cols, exact=True)
+    _gpu(scales, "scales", (torch.uint8,), dev, rows * (cols // 32))
+    _gpu(nonfinite, "nonfinite", (torch.int32,), dev, 1, optional=True)
+    _call(dev, "fp8_quantize_mx", lib().fp8_quantize_mx, _ptr(x), dt, rows, cols, int(fmt),
+          _ptr(codes), _ptr(scales), _ptr(nonfinite), _stream(stream, dev))
     return codes, scales
 
 
 def fp8_dequantize_mx(codes, fmt: int, scales, out=None, stream=None):
     """decode(code) * 2^(byte - 127) in float32; returns out [rows, cols]."""
     import torch
-    if codes.dim() != 2 or codes.dtype != torch.uint8:
-        raise TypeError("codes must be a 2-D uint8 tensor")
-    rows, cols = codes.shape
+    rows, cols, dev = _matrix(codes, "codes", (torch.uint8,))
+    _gpu(scales, "scales", (torch.uint8,), dev, rows * (cols // 32))
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
-    _check(lib().fp8_dequantize_mx(_ptr(codes), rows, cols, int(fmt), _ptr(scales), _ptr(out),
-                                   _stream(stream)), "fp8_dequantize_mx")
+        out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    _gpu(out, "out", (torch.float32,), dev, rows * cols, exact=True)
+    _call(dev, "fp8_dequantize_mx", lib().fp8_dequantize_mx, _ptr(codes), rows, cols, int(fmt),
+          _ptr(scales), _ptr(out), _stream(stream, dev))
     return out
