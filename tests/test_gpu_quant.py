@@ -166,6 +166,29 @@ def test_dequantize_all_codes_all_granularities(dev):
                 assert np.array_equal(_u32(out), ref.reshape(-1).view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols", [(128, 128), (1152, 384), (256, 5248), (384, 6016),
+                                       (640, 3968), (256, 18432)])
+def test_dequantize_128x128_tile_lookup(rows, cols, dev):
+    """The 128x128 dequantizers walk the codes in row-major order and find
+    each group's tile from its position: one row per work item or many
+    (narrow matrices), and block counts per row (41 for 5248 columns, 47 for
+    6016) where the FP32 quotient needs its one-off correction.  Every tile
+    has its own scale, so a wrong tile shows."""
+    rng = np.random.default_rng(rows * 7 + cols)
+    codes = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+    ns = oracle.n_scales(rows, cols, B128)
+    sc = np.ldexp(rng.uniform(1.0, 2.0, ns), rng.integers(-20, 20, ns)).astype(np.float32)
+    c = torch.from_numpy(codes).to(dev)
+    s = torch.from_numpy(sc).to(dev)
+    for fmt in (E4M3, E5M2):
+        out = gs.fp8_dequantize(c, fmt, B128, s)
+        out16 = gs.fp8_dequantize_bf16(c, fmt, B128, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(_u32(out), oracle.dequantize(codes, fmt, B128, sc).reshape(-1).view(np.uint32))
+        assert np.array_equal(out16.view(torch.int16).cpu().numpy().view(np.uint16),
+                              oracle.dequantize_bf16(codes, fmt, B128, sc))
+
+
 def test_tiny_per_tensor_case(dev):
     """1024x1024 BF16 N(0,1) per-tensor E4M3 and its dequantization."""
     q = synth.tiny_quant()
