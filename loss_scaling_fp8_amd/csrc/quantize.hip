@@ -151,10 +151,14 @@ struct LaneData {
             amax_bits = m16 << 16;
             return nf;
         } else {
-            uint32_t m = 0;
+            // the maximum of the bits shifted left by one (the sign dropped,
+            // the order kept): written unlike the fallback's |x| below, so
+            // that the compiler does not keep every |x| alive for it
+            uint32_t m2 = 0;
 #pragma unroll
-            for (int i = 0; i < kWords; ++i) m = max(m, w[i] & 0x7FFFFFFFu);
-            const bool nf = m >= 0x7F800000u;
+            for (int i = 0; i < kWords; ++i) m2 = max(m2, w[i] << 1);
+            const bool nf = m2 >= (0x7F800000u << 1);
+            uint32_t m = m2 >> 1;
             if (nf) {
                 m = 0;
 #pragma unroll
@@ -306,8 +310,13 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const int64_t ti = t / tiles_per_row, tj = t - ti * tiles_per_row;
         const int64_t base = (ti * 128 + row0) * cols + tj * 128 + seg * kPerVec;
+        // the row stride, opaque per tile: keeps the compiler from hoisting
+        // one 64-bit address per pass out of the tile loop (32 VGPRs with
+        // FP32 input)
+        int64_t rs = int64_t(kRowsPerPass) * cols;
+        __asm__ volatile("" : "+s"(rs));
         LaneData<IN, kPasses> L;
-        L.template load_strided<GS_Q128_NT_LOAD>(x + base, int64_t(kRowsPerPass) * cols);
+        L.template load_strided<GS_Q128_NT_LOAD>(x + base, rs);
         uint32_t amax_bits;
         const bool nf = L.absmax(amax_bits);
         saw_nf |= nf;
@@ -331,7 +340,7 @@ void quant_128x128_kernel(const IN *__restrict__ x, int64_t cols, int64_t tiles_
         constexpr int kWordsPerPass = kPerVec / 4;
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            uint8_t *dst = codes + base + int64_t(p) * kRowsPerPass * cols;
+            uint8_t *dst = codes + base + int64_t(p) * rs;
             if constexpr (kWordsPerPass == 2)
                 st<GS_Q128_NT_STORE>(dst, u32x2{out[2 * p], out[2 * p + 1]});
             else
