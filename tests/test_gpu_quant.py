@@ -189,6 +189,29 @@ def test_dequantize_128x128_tile_lookup(rows, cols, dev):
                               oracle.dequantize_bf16(codes, fmt, B128, sc))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_empty_matrices(dtype, dev):
+    """Empty inputs at every granularity: nothing is written except the
+    per-tensor scale, which an empty tensor still gets (the floor scale, as
+    the oracle computes it), both formats."""
+    for fmt in (E4M3, E5M2):
+        for gran, shape in ((PT, (0, 5)), (PT, (7, 0)), (B1, (0, 256)), (B128, (0, 128)),
+                            (B128, (128, 0)), (B32, (0, 64))):
+            x = torch.empty(shape, dtype=dtype, device=dev)
+            codes = torch.empty(shape, dtype=torch.uint8, device=dev)
+            ns = oracle.n_scales(*shape, gran)
+            sc = torch.full((max(ns, 1),), -1.0, device=dev)
+            gs.fp8_quantize(x, fmt, gran, gs.FP8_SCALE_FROM_AMAX, codes, sc)
+            out = gs.fp8_dequantize(codes, fmt, gran, sc)
+            torch.cuda.synchronize()
+            assert out.shape == shape
+            if gran == PT:
+                _, rs, _ = oracle.quantize(np.zeros(shape, np.float32), fmt, gran)
+                assert _u32(sc)[0] == rs.reshape(-1).view(np.uint32)[0]
+            else:
+                assert float(sc[0].item()) == -1.0
+
+
 def test_tiny_per_tensor_case(dev):
     """1024x1024 BF16 N(0,1) per-tensor E4M3 and its dequantization."""
     q = synth.tiny_quant()
