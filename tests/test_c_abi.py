@@ -1,6 +1,7 @@
 """The C ABI from C: tests/c/abi_host.c is compiled as strict C99 against
 include/gs.h, linked against the built libgsfp8.so, and run (host-only
-entry points and argument checks; no GPU needed)."""
+entry points and argument checks; no GPU needed); tests/c/abi_gpu.c, the C
+caller the GPU tests run, is compiled and linked."""
 import os
 import shutil
 import subprocess
@@ -26,3 +27,14 @@ def test_c99_caller(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "0 failure(s)" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_c_gpu_caller_builds(tmp_path):
+    """tests/c/abi_gpu.c (run by the GPU tests) compiles as strict C11
+    against include/gs.h and links against the built library, the oracle
+    and the HIP runtime; nothing is run here."""
+    import runpy
+    mod = runpy.run_path(os.path.join(ROOT, "tests", "c", "build_abi_gpu.py"))
+    exe = mod["build"](str(tmp_path / "abi_gpu"))
+    assert os.path.exists(exe)
