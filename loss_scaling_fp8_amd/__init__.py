@@ -104,9 +104,9 @@ def _gpu(t, name: str, dtypes, dev=None, numel: int | None = None, exact: bool =
         raise ValueError("%s is required" % name)
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on a GPU, not on %s" % (name, t.device))
-    if dev is not None and t.device != dev:
+    if dev is not None and t.get_device() != dev.index:
         raise ValueError("%s is on %s, the other arguments on %s" % (name, t.device, dev))
     if t.dtype not in dtypes:
         raise TypeError("%s must be %s, not %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
@@ -123,10 +123,14 @@ def _bytes(t) -> int:
 
 
 def _stream(stream, dev) -> int | None:
-    """The HIP stream handle: torch's current stream on dev by default; a
-    torch stream must belong to dev; an integer is passed as is."""
+    """The HIP stream handle: torch's current stream on dev by default (read
+    as a raw handle where torch offers that, without building a Stream
+    object); a torch stream must belong to dev; an integer is passed as is."""
     import torch
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(dev.index)
         return torch.cuda.current_stream(dev).cuda_stream
     if hasattr(stream, "cuda_stream"):
         if stream.device != dev:
@@ -139,8 +143,11 @@ def _call(dev, where: str, fn, *args) -> None:
     """Calls a C entry point with the tensors' device current (the unscale's
     descriptor cache allocates on the current device) and raises on error."""
     import torch
-    with torch.cuda.device(dev):
+    if dev.index == torch.cuda.current_device():
         status = fn(*args)
+    else:
+        with torch.cuda.device(dev):
+            status = fn(*args)
     _check(status, where)
 
 
@@ -209,12 +216,13 @@ def _grad_lists(grads, outs, dev):
     n = len(grads)
     if len(outs) != n:
         raise ValueError("grads and outs differ in length")
+    di = dev.index
     for g, o in zip(grads, outs):
         if not isinstance(g, torch.Tensor) or not isinstance(o, torch.Tensor):
             raise TypeError("grads and outs must be torch tensors")
         if g.dtype != torch.float16 or o.dtype != torch.float32:
             raise TypeError("grads must be float16 and outs float32")
-        if g.device != dev or o.device != dev:
+        if not (g.is_cuda and o.is_cuda) or g.get_device() != di or o.get_device() != di:
             raise ValueError("every gradient and output must be on %s (the scale's device)" % dev)
         if o.numel() != g.numel() or not g.is_contiguous() or not o.is_contiguous():
             raise ValueError("each out must be a contiguous float32 tensor of its grad's size")
