@@ -233,9 +233,10 @@ gs_status gs_update_scale_hysteresis(float *scale, int32_t *growth_tracker,
  * fp8_quantize_workspace_size -- bytes of device workspace fp8_quantize
  * needs for this shape and granularity in FP8_SCALE_FROM_AMAX mode: 32 KiB of
  * per-workgroup partial maxima for per-tensor scaling (the scale depends on
- * the whole tensor: one pass writes the partial maxima, one workgroup turns
- * them into the scale, a third pass casts); block granularities need none.
- * Returns 0 when no workspace is needed.
+ * the whole tensor: one pass writes the partial maxima, then the cast pass
+ * derives the scale from them -- every cast workgroup itself for a tensor of
+ * at most 192 MiB, one extra workgroup beforehand for a larger one); block
+ * granularities need none.  Returns 0 when no workspace is needed.
  */
 size_t fp8_quantize_workspace_size(int64_t rows, int64_t cols, fp8_granularity g);
 
