@@ -23,13 +23,20 @@
 //  * 128x128: one 256-lane workgroup per tile, the whole tile held in
 //    registers (64 elements per lane); amax by DPP inside rows of 16 lanes,
 //    two cross-row shuffles, and 4 LDS words across the waves.
-//  * per-tensor: the scale depends on the whole tensor, so three launches:
-//    a pass writes one partial max per workgroup (<= 8192; no atomics, no
-//    zero-initialised memory), one 1024-lane workgroup turns them into the
-//    scale, and the cast pass streams the tensor again.  Both passes use the
-//    1x128 lane layout (a lane owns 32 contiguous elements).  Delayed
-//    scaling casts with the previous scale and emits the partials in the
-//    same pass, then updates the history in one workgroup.
+//  * per-tensor: the scale depends on the whole tensor, so the tensor is
+//    read twice: a pass writes one partial max per workgroup (<= 8192; no
+//    atomics, no zero-initialised memory), then the cast pass streams the
+//    tensor again.  For a tensor that fits in the infinity cache the amax
+//    pass writes at most 1024 partials and every cast workgroup reduces
+//    them itself; a larger one has one 1024-lane workgroup turn them into
+//    the scale in between.  Both passes use the 1x128 lane layout (a lane
+//    owns 32 contiguous elements).  Delayed scaling casts with the previous
+//    scale and emits the partials in the same pass, then updates the
+//    history in one workgroup.
+//  * dequantize: a flat walk over groups of codes (4 per lane with FP32
+//    output, 8 with BF16), each lane one 16-byte store, so every wave-wide
+//    store writes 1 KiB of contiguous output; 128x128 finds each group's
+//    tile from its position.
 //  * Division: x / s is formed from r = fl32(1/s) and one FMA correction
 //    (div_by_scale) whenever s is in the range where that reproduces the
 //    IEEE quotient's FP8 code, else by IEEE division (only a given scale
