@@ -15,6 +15,12 @@ the other kernels' times from the same steps run again after it, untimed,
 with events around every launch.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
+                    [--no-ceilings] [--all-configs]
+
+After the step, `ceilings` gives the best rate of each access pattern the
+kernels use (read, write, 2 B -> 4 B, 2 B -> 1 B, 1 B -> 4 B) at the
+kernels' own sizes, from the streaming kernels of libgsceil.so, and every
+kernel's `frac_of_ceiling` against its pattern.
 
 Prints one JSON line.  More than one GPU is not supported (this path is
 measured on one GPU; see the sharding notes in the design document).
@@ -71,6 +77,32 @@ def pmc_traffic(src_hash):
         return None
 
 
+def cpu_share():
+    """(threads, host_cores, quota_cores): the cores in this process's
+    affinity mask, limited by the cgroup CPU quota and by OMP_NUM_THREADS
+    when either is set -- the CPU share a job on a shared GPU host is given
+    (more threads than that only queue for the same cores)."""
+    try:
+        host = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host = os.cpu_count() or 1
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as fh:
+            q, period = fh.read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    threads = host
+    if quota is not None:
+        threads = min(threads, quota)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    return max(1, threads), host, quota
+
+
 def cpu_baseline(grad_sample, act_rows, wgt_rows):
     """The oracle (plain C, untouched) on a bounded sample of the same
     workload, inputs being host copies of the device tensors: once on one
@@ -104,11 +136,7 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
     for fn, a in jobs:
         fn(*a)
     t_one = time.perf_counter() - t0
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    threads = max(1, min(16, ncpu))
+    threads, host_cores, quota = cpu_share()
     runs = []
     with ThreadPoolExecutor(threads) as ex:
         for _ in range(3):
@@ -118,12 +146,17 @@ def cpu_baseline(grad_sample, act_rows, wgt_rows):
     t_all = float(np.median(runs))
     return {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "value_1_core": round(nbytes / t_one / 1e9, 4),
+            "host_cores": host_cores, "cgroup_cpu_quota": quota,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": "%d FP16 elements (embedding + lm_head gradients) unscaled, %dx%d "
                       "activation rows 1x128 and %dx%d weight rows 128x128 quantized and "
                       "dequantized, E4M3; the C oracle on %d threads (median of 3 runs, "
-                      "%.1f s) and on 1 (%.1f s)"
+                      "%.1f s) and on 1 (%.1f s); %d cores in the affinity mask, the "
+                      "threads limited to this job's CPU share (cgroup quota, "
+                      "OMP_NUM_THREADS)"
                       % (grad_sample.size, act_rows.shape[0], act_rows.shape[1],
-                         wgt_rows.shape[0], wgt_rows.shape[1], threads, t_all, t_one)}
+                         wgt_rows.shape[0], wgt_rows.shape[1], threads, t_all, t_one,
+                         host_cores)}
 
 
 class TimingEvents:
@@ -168,6 +201,88 @@ class TimingEvents:
         for e in self.events:
             self.hip.hipEventDestroy(e)
         self.events = []
+
+
+CEIL_LIB = os.path.join(ROOT, "loss_scaling_fp8_amd", "libgsceil.so")
+CEIL_PATTERNS = {"read": 0, "write": 1, "expand_2to4": 2, "narrow_2to1": 3, "expand_1to4": 4}
+CEIL_POLICY = ("plain", "nt", "sc1nt")
+
+
+def measure_ceilings(dev, specs, tev, reps=5):
+    """Best rate of each access pattern over a sweep of launch shapes, from
+    the streaming kernels of libgsceil.so on flat buffers of the given
+    sizes.  specs: (name, pattern, n) with n elements (read / write: bytes).
+    Each variant is launched once untimed, then `reps` times, each launch
+    between two HIP events on the current stream (the events of the
+    unscale's own timing); the median is the variant's time, the fastest
+    variant the ceiling.  Working sets below 512 MB would otherwise be
+    served partly by the 256 MB infinity cache on a repeat, so each of
+    their launches follows a 1 GiB write and a 1 GiB read (stream-ordered,
+    untimed): their inputs come from HBM, like those of the benchmark
+    step's kernels, which follow the 48 GB unscale."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    L = ctypes.CDLL(CEIL_LIB)
+    L.gsc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_void_p]
+    junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        junk.fill_(1.0)
+        junk_rd.sum()
+    L.gsc_stream.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, pattern, n in specs:
+        p = CEIL_PATTERNS[pattern]
+        src_bytes = {0: n, 1: 0, 2: 2 * n, 3: 2 * n, 4: n}[p]
+        dst_bytes = {0: 1024, 1: n, 2: 4 * n, 3: n, 4: 4 * n}[p]
+        src = torch.empty(max(src_bytes, 16), dtype=torch.uint8, device=dev)
+        dst = torch.empty(dst_bytes, dtype=torch.uint8, device=dev)
+        moved = src_bytes + (0 if p == 0 else dst_bytes)
+        cold = src_bytes + dst_bytes < (512 << 20)
+        best = None
+        for unroll in (1, 2, 4, 8):
+            for ntl in (0, 1):
+                if p == 1 and ntl:
+                    continue                       # no loads to vary
+                for policy in range(3):
+                    if p == 0 and policy:
+                        continue                   # no stores to vary
+                    for occ in (0, 7, 5):
+                        args = (p, src.data_ptr(), dst.data_ptr(), n, unroll, ntl, policy, occ,
+                                stream)
+                        rc = L.gsc_stream(*args)
+                        if rc != 0:
+                            raise RuntimeError("gsc_stream%r returned %d" % (args[:1] + args[3:8], rc))
+                        evs = [(tev.new(), tev.new()) for _ in range(reps)]
+                        for a, b in evs:
+                            if cold:
+                                flush()
+                            tev.record(a, stream)
+                            L.gsc_stream(*args)
+                            tev.record(b, stream)
+                        torch.cuda.synchronize()
+                        ms = float(np.median([tev.elapsed_ms(a, b) for a, b in evs]))
+                        if best is None or ms < best[0]:
+                            best = (ms, unroll, ntl, policy, occ)
+        ms, unroll, ntl, policy, occ = best
+        out[name] = {"GBps": round(moved / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4),
+                     "bytes": moved, "elements": n, "pattern": pattern,
+                     "inputs": "from HBM (flushed before each launch)" if cold else
+                               "from HBM (working set far above the caches)",
+                     "variant": "unroll %d, %s loads, %s stores, %s" % (
+                         unroll, "non-temporal" if ntl else "plain", CEIL_POLICY[policy],
+                         "no occupancy cap" if occ == 0 else "%d workgroups per CU" % occ)}
+        log("ceiling %s: %.0f GB/s (%s)" % (name, out[name]["GBps"], out[name]["variant"]))
+        del src, dst
+        torch.cuda.empty_cache()
+    del junk, junk_rd
+    return out
 
 
 def _time_launches(fn, reps, flush=None):
@@ -278,31 +393,74 @@ def measure_configs(dev):
         del x, codes, scales, out
     res["per_tensor_8192"] = pt
     # 4 GiB special values, scales from the block amax
+    sv = measure_special_values(dev, [sp.name for sp in synth.special_values_4gib()],
+                                ("e4m3", "e5m2"), ("cold", "b2b"), 20)
+    res["special_4gib"] = sv
+    return res
+
+
+def measure_special_values(dev, tensors, fmts, phases, reps):
+    """The four 16384x32768 BF16 special-value tensors: quantize with scales
+    from the amax (per-tensor, 1x128, 128x128) and the FP32 dequantize, per
+    tensor x format x granularity, `reps` launches each.  Phase "cold": a
+    1 GiB write and a 1 GiB read (stream-ordered, untimed) before every
+    launch, so that the previous launch's writes have drained and the cache
+    holds clean lines of other data; phase "b2b": the launches back to back,
+    each paying for the previous one's write drain.  Medians of HIP-event
+    times; GB/s from the algorithmic bytes."""
+    import torch
+
+    import loss_scaling_fp8_amd as gs
+    import synth
+
+    junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        junk.fill_(1.0)
+        junk_rd.sum()
+
+    fmt_id = {"e4m3": gs.FP8_E4M3, "e5m2": gs.FP8_E5M2}
+    grans = ((gs.FP8_PER_TENSOR, "tensor"), (gs.FP8_BLOCK_1x128, "1x128"),
+             (gs.FP8_BLOCK_128x128, "128x128"))
     sv = {}
     for sp in synth.special_values_4gib():
+        if sp.name not in tensors:
+            continue
         x = sp.full(dev)
         n = sp.rows * sp.cols
         codes = torch.empty((sp.rows, sp.cols), dtype=torch.uint8, device=dev)
         out = torch.empty((sp.rows, sp.cols), dtype=torch.float32, device=dev)
         ws = torch.empty(gs.fp8_quantize_workspace_size(sp.rows, sp.cols, gs.FP8_PER_TENSOR),
                          dtype=torch.uint8, device=dev)
-        for fmt in (gs.FP8_E4M3, gs.FP8_E5M2):
-            for gran, gname in ((gs.FP8_PER_TENSOR, "tensor"), (gs.FP8_BLOCK_1x128, "1x128"),
-                                (gs.FP8_BLOCK_128x128, "128x128")):
+        for fname in fmts:
+            fmt = fmt_id[fname]
+            for gran, gname in grans:
                 sc = torch.empty(gs.scale_shape(sp.rows, sp.cols, gran), dtype=torch.float32,
                                  device=dev)
                 gs.fp8_quantize(x, fmt, gran, 0, codes, sc, None, ws)
-                mq, _ = _time_launches(lambda: gs.fp8_quantize(x, fmt, gran, 0, codes, sc, None,
-                                                               ws), 5)
-                md, _ = _time_launches(lambda: gs.fp8_dequantize(codes, fmt, gran, sc, out), 5)
                 ns = sc.numel()
-                key = "%s/%s/%s" % (sp.name, "e4m3" if fmt == 0 else "e5m2", gname)
-                sv[key] = {"quant_GBps": round((n * 3 + ns * 4) / mq / 1e6, 1),
-                           "dequant_GBps": round((n * 5 + ns * 4) / md / 1e6, 1)}
+                bq, bd = n * 3 + ns * 4, n * 5 + ns * 4
+                for phase in phases:
+                    fl = flush if phase == "cold" else None
+                    mq, mq_min = _time_launches(
+                        lambda: gs.fp8_quantize(x, fmt, gran, 0, codes, sc, None, ws), reps, fl)
+                    md, md_min = _time_launches(
+                        lambda: gs.fp8_dequantize(codes, fmt, gran, sc, out), reps, fl)
+                    key = "%s/%s/%s/%s" % (sp.name, fname, gname, phase)
+                    sv[key] = {"quant_ms": round(mq, 4), "quant_GBps": round(bq / mq / 1e6, 1),
+                               "quant_GBps_best": round(bq / mq_min / 1e6, 1),
+                               "dequant_ms": round(md, 4),
+                               "dequant_GBps": round(bd / md / 1e6, 1),
+                               "dequant_GBps_best": round(bd / md_min / 1e6, 1)}
+                    log("%s: quant %.0f GB/s, dequant %.0f GB/s" %
+                        (key, sv[key]["quant_GBps"], sv[key]["dequant_GBps"]))
+                del sc
         del x, codes, out
         torch.cuda.empty_cache()
-    res["special_4gib"] = sv
-    return res
+    sv["note"] = ("per-tensor runs two passes over the input (amax, then cast): its GB/s "
+                  "counts the algorithmic 3 B/element, the traffic is 5 B/element")
+    return sv
 
 
 def main():
@@ -311,9 +469,16 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming-kernel ceilings (about 5 s)")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time the tiny, per-tensor 8192^2 and 4 GiB special-value "
                          "configurations (reported under \"configs\")")
+    ap.add_argument("--special-values", nargs=3, metavar=("TENSOR", "FMT", "PHASE"),
+                    help="only time the 4 GiB special-value quantize/dequantize for one "
+                         "tensor (mix, anchored, saturation, random), format (e4m3, e5m2) "
+                         "and phase (cold, b2b), 20 launches each (for per-configuration "
+                         "kernel-trace profiles); prints one JSON object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 6 plain copy kernels of 1 GiB (for HBM counter calibration)")
     ap.add_argument("--extensions", "--sumsq", dest="extensions", action="store_true",
@@ -338,6 +503,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.special_values:
+        t, f, ph = args.special_values
+        if t not in ("mix", "anchored", "saturation", "random") or f not in ("e4m3", "e5m2") \
+                or ph not in ("cold", "b2b"):
+            ap.error("--special-values TENSOR FMT PHASE: see --help")
+        gs.lib()
+        print(json.dumps({"special_4gib": measure_special_values(dev, (t,), (f,), (ph,), 20)}))
+        return
     if args.copy_calibration:
         # int32 -> float32 converting copy: an elementwise kernel reading and
         # writing 4 bytes per element (a same-type copy would be a memcpy)
@@ -458,7 +631,7 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
-    state, copy_gbps = (None, None, None), None
+    state = (None, None, None)
     if not args.pmc_safe:
         state = (float(S.item()), int(tracker.item()), int(skips.item()))
         log("final S=%g tracker=%d skips=%d" % state)
@@ -472,28 +645,32 @@ def main():
     torch.cuda.synchronize()
     for j, n in enumerate(names[1:], 1):
         per_kernel_ms[n] = mean_ms(events_all, j)
+    ceilings = None
+    if not args.pmc_safe and not args.no_ceilings:
+        # achievable rate of each access pattern at the kernels' own sizes
+        # (flat buffers, outside the step; about 50 GB more of HBM)
+        ceilings = measure_ceilings(dev, [
+            ("read", "read", n_grad * 2), ("write", "write", n_grad * 4),
+            ("expand_2to4", "expand_2to4", n_grad),
+            ("narrow_2to1_act", "narrow_2to1", n_a), ("narrow_2to1_wgt", "narrow_2to1", n_w),
+            ("expand_1to4_act", "expand_1to4", n_a), ("expand_1to4_wgt", "expand_1to4", n_w)],
+            tev)
     tev.destroy()
-    if not args.pmc_safe:
-        # copy ceiling: a plain device copy of 1 GiB (2 GiB moved), outside the step
-        src = outs[0].view(-1)[: 1 << 28]
-        cbuf = torch.empty_like(src)
-        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cbuf.copy_(src)
-        ce0.record()
-        for _ in range(5):
-            cbuf.copy_(src)
-        ce1.record()
-        torch.cuda.synchronize()
-        copy_gbps = round(5 * 2 * src.numel() * 4 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9, 1)
 
     kbytes = {"unscale_check": bytes_unscale, "update_scale": bytes_update,
               "quant_1x128": bytes_qa, "quant_128x128": bytes_qw,
               "dequant_1x128": bytes_da, "dequant_128x128": bytes_dw}
+    kceil = {"unscale_check": "expand_2to4", "quant_1x128": "narrow_2to1_act",
+             "quant_128x128": "narrow_2to1_wgt", "dequant_1x128": "expand_1to4_act",
+             "dequant_128x128": "expand_1to4_wgt"}
     kernels = {}
     for n in names:
         gbps = kbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9
         kernels[n] = {"ms": round(per_kernel_ms[n], 4), "bytes": kbytes[n],
                       "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
+        if ceilings and n in kceil:
+            kernels[n]["ceiling"] = kceil[n]
+            kernels[n]["frac_of_ceiling"] = round(gbps / ceilings[kceil[n]]["GBps"], 4)
 
     # unscale fused with the exact gradient sum of squares, on the same
     # resident gradient set (outside the timed step; own HIP events)
@@ -569,7 +746,8 @@ def main():
     un = kernels["unscale_check"]
     roofline = {"bound": "hbm", "achieved": un["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(un["GBps"] / PEAK_GBPS, 4), "traffic": pmc_traffic(src_hash),
-                "kernel": "unscale_check_kernel", "algorithmic_bytes_per_launch": bytes_unscale}
+                "kernel": "unscale_check_kernel", "algorithmic_bytes_per_launch": bytes_unscale,
+                "frac_of_ceiling": un.get("frac_of_ceiling")}
 
     result = {
         "metric": METRIC,
@@ -593,7 +771,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "extensions": ext,
-        "copy_ceiling_GBps": copy_gbps,
+        "ceilings": ceilings,
         "final_state": {"S": state[0], "tracker": state[1], "skips": state[2]},
     }
     if not args.no_cpu_baseline and not args.pmc_safe:

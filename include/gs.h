@@ -10,18 +10,33 @@
  * a repeated call with the same arguments.  Device buffers must stay alive
  * until the enqueued work has finished.  The one exception is the first
  * call of gs_unscale_check / gs_unscale_check_sumsq with a new gradient
- * list: it allocates the list's chunk descriptors and uploads them with a
- * blocking copy (and evicting an old list from the cache waits for the
- * device); repeated calls with the same list do neither.  After that first
- * call every entry point can be captured in a HIP graph: none allocates,
- * copies from the host or records a memset.
+ * list: it takes device memory for the list's chunk descriptors and uploads
+ * them on an internal stream, waiting for that upload only; repeated calls
+ * with the same list do neither.  After that first call every entry point
+ * can be captured in a HIP graph: none allocates, copies from the host or
+ * records a memset.
+ *
+ * Descriptor lifetime: the library caches the descriptors of at most 64
+ * lists / 1 GiB and evicts the least recently used list when a new one does
+ * not fit.  Eviction never frees memory or waits for the device: the
+ * evicted buffer is reused for a later list once every kernel that read it
+ * has finished (tracked by an event per stream).  A list used by a call
+ * made while its stream was capturing a graph is never evicted, so a
+ * captured graph may be replayed at any later time; such lists stay cached
+ * until the process ends.  Idle retired buffers beyond 1 GiB per device are
+ * freed (hipFree, which synchronises the device), which happens only when
+ * callers keep creating lists larger than every retired one.
  *
  * Threads: entry points may be called from several host threads at once
  * (each on its own stream, or the same one).  The descriptor cache is
  * locked, and an unscale call enqueues its kernel while holding that lock,
- * so no thread's eviction can free a list between another thread's lookup
- * and its launch.  Calls whose device outputs or workspaces overlap must be
- * ordered by the caller (streams or events), as for any asynchronous work.
+ * so no thread's eviction can retire a list between another thread's lookup
+ * and its launch.  Another thread may capture a graph meanwhile when its
+ * capture mode permits this thread's first call with a new list (HIP's
+ * thread-local or relaxed capture modes), since that call allocates and
+ * synchronises its own upload stream.  Calls whose device outputs or
+ * workspaces overlap must be ordered by the caller (streams or events), as
+ * for any asynchronous work.
  *
  * Errors: argument errors are detected on the host and returned before
  * anything is enqueued, with no side effects.  Non-finite DATA is never an
@@ -98,11 +113,11 @@ typedef enum { FP8_SCALE_FROM_AMAX = 0, FP8_SCALE_GIVEN = 1 } fp8_scale_mode;
  *   stream     hipStream_t.
  * The list is cut into 2048-element chunks whose descriptors (addresses and
  * sizes) are built on the first call with a given (grads, outs, numels) list
- * and cached on the device (at most 64 lists / 1 GiB, least recently used
- * evicted; an eviction waits for the device), so a repeated call with the
- * same list uploads nothing.  That first call allocates and uploads
- * synchronously (the upload has finished when the call returns).  Device addresses must lie below 2^48
- * (GS_ERR_ARG otherwise; every current AMD GPU address does).
+ * and cached on the device (lifetime rules at the top of this file), so a
+ * repeated call with the same list uploads nothing.  That first call
+ * uploads synchronously (the upload has finished when the call returns).
+ * Device addresses must lie below 2^48 (GS_ERR_ARG otherwise; every current
+ * AMD GPU address does).
  */
 gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *outs,
                            const int64_t *numels, gs_dtype in_dtype, const float *scale,

@@ -1,9 +1,12 @@
-"""Build libgsfp8.so (the HIP library behind include/gs.h) for gfx950.
+"""Build libgsfp8.so (the HIP library behind include/gs.h) for gfx950, and
+libgsceil.so (the streaming kernels the benchmark measures its ceilings
+with; not part of the library).
 
     python -m loss_scaling_fp8_amd.build
 
 Each csrc/*.hip file is compiled to an object in parallel, then linked into
-loss_scaling_fp8_amd/libgsfp8.so.  Packed FP32 instructions are disabled for
+loss_scaling_fp8_amd/libgsfp8.so; ceilings/*.hip are linked into
+loss_scaling_fp8_amd/libgsceil.so.  Packed FP32 instructions are disabled for
 all device code (-Xclang -target-feature -Xclang -packed-fp32-ops; the host
 pass warns that it does not know the feature, which is harmless).
 """
@@ -20,6 +23,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgsfp8.so")
+CEIL_DIR = os.path.join(PKG, "ceilings")
+CEIL_LIB = os.path.join(PKG, "libgsceil.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -35,6 +40,10 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def ceiling_sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CEIL_DIR, "*.hip")))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CXXFLAGS, "-c", src, "-o", obj]
@@ -44,20 +53,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library (always)."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(min(len(srcs), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link both shared libraries (always)."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs, csrcs = sources(), ceiling_sources()
+    with ThreadPoolExecutor(min(len(srcs) + len(csrcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs + csrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], CEIL_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEIL_LIB)
     return LIB
 
 

@@ -1,9 +1,9 @@
 // api.hip -- the C ABI of libgsfp8 (declared in include/gs.h): argument
 // validation on the host, the cached per-chunk descriptors of the
 // multi-tensor unscale, and dispatch to the kernels.  No entry point
-// synchronises the host or reads device memory; the only device allocation
-// happens the first time a given gradient list is seen (its descriptors are
-// cached).
+// synchronises the device or reads device memory; device memory is taken
+// only the first time a given gradient list is seen (its descriptors are
+// cached, and that first call waits for their upload).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -23,27 +23,60 @@ constexpr int64_t kMaxDim = int64_t(1) << 31;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 // ------------------------------------------------------------ work-list cache
-// Key: device id + the (input, output, numel) triplets.  Value: one device
-// allocation holding the per-chunk descriptors.  Least-recently-used
-// eviction by count and by bytes; an evicted list may still be referenced by
-// queued kernels, so eviction waits for the list's device before freeing.
+// Key: device id + the (input, output, numel) triplets.  Value: a device
+// buffer holding the per-chunk descriptors, and one event per stream that
+// has launched a kernel reading it, re-recorded after every such launch.
 // A caller enqueues its kernel while holding the cache lock (with_list), so
 // no list can be evicted between its lookup and the launch that reads it.
-struct CachedList {
+//
+// No call frees device memory or waits for the device (hipFree would
+// synchronise the whole device, behind every other thread's queued work,
+// and is not allowed while another thread captures a graph):
+//  * the least recently used lists are evicted by count and by bytes.  An
+//    evicted list's buffer is retired together with its events; a later
+//    list takes it over (best fit, at most twice the size it needs) once
+//    hipEventQuery reports every event complete.  Only when the retired
+//    buffers of a device exceed kCacheBytes are the idle ones freed, which
+//    happens when callers keep creating lists larger than any retired one;
+//  * a list launched while its stream is capturing a graph is pinned: the
+//    graph holds the descriptor address and may be replayed at any later
+//    time, so that list is never evicted;
+//  * uploads go through an internal non-blocking stream per device and wait
+//    for that stream only.
+struct DevBuffer {
     void *dev = nullptr;
-    int64_t nchunks = 0;
-    size_t bytes = 0;
+    size_t cap = 0;
     int device = 0;
+};
+
+struct StreamUse {
+    hipStream_t stream;
+    hipEvent_t event;
+};
+
+struct CachedList {
+    DevBuffer buf;
+    int64_t nchunks = 0;
+    bool pinned = false;
+    std::vector<StreamUse> uses;
+};
+
+struct Retired {
+    DevBuffer buf;
+    std::vector<StreamUse> uses;
 };
 
 constexpr size_t kCacheEntries = 64;
 constexpr size_t kCacheBytes = size_t(1) << 30;
+constexpr size_t kBufferGranule = size_t(64) << 10;
 
 struct ListCache {
     std::mutex mu;
-    size_t bytes = 0;
-    std::list<std::string> lru;   // front = most recent
+    size_t bytes = 0;                          // capacity of the cached lists
+    std::list<std::string> lru;                // front = most recent
     std::unordered_map<std::string, std::pair<CachedList, std::list<std::string>::iterator>> map;
+    std::list<Retired> retired;                // front = most recently retired
+    std::unordered_map<int, hipStream_t> upload_stream;
 };
 
 ListCache &cache() {
@@ -95,64 +128,169 @@ gs_status make_descriptors(int32_t n, const void *const *in, float *const *out,
     return GS_OK;
 }
 
-gs_status build_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
-                     CachedList &cl) {
-    std::vector<gsk::ChunkDesc> host;
-    const gs_status st = make_descriptors(n, in, out, numel, host);
-    if (st != GS_OK) return st;
-    const int64_t total = int64_t(host.size());
-    const size_t bytes = host.size() * sizeof(gsk::ChunkDesc);
-    void *dev = nullptr;
-    if (hipMalloc(&dev, bytes) != hipSuccess) return GS_ERR_HIP;
-    if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipFree(dev);
-        return GS_ERR_HIP;
+// True when every kernel that read the buffer has finished.
+bool uses_done(const std::vector<StreamUse> &uses) {
+    for (const StreamUse &u : uses)
+        if (hipEventQuery(u.event) != hipSuccess) return false;
+    return true;
+}
+
+void destroy_uses(std::vector<StreamUse> &uses) {
+    for (StreamUse &u : uses) (void)hipEventDestroy(u.event);
+    uses.clear();
+}
+
+// A buffer of at least `need` bytes on `device`: an idle retired one (best
+// fit, at most twice the size), else a new allocation.
+gs_status take_buffer(ListCache &c, int device, size_t need, DevBuffer &out) {
+    auto best = c.retired.end();
+    for (auto it = c.retired.begin(); it != c.retired.end(); ++it) {
+        if (it->buf.device != device || it->buf.cap < need || it->buf.cap > 2 * need) continue;
+        if (best != c.retired.end() && it->buf.cap >= best->buf.cap) continue;
+        if (!uses_done(it->uses)) continue;
+        best = it;
     }
-    cl.dev = dev;
-    cl.nchunks = total;
-    cl.bytes = bytes;
+    if (best != c.retired.end()) {
+        out = best->buf;
+        destroy_uses(best->uses);
+        c.retired.erase(best);
+        return GS_OK;
+    }
+    const size_t cap = (need + kBufferGranule - 1) / kBufferGranule * kBufferGranule;
+    void *dev = nullptr;
+    if (hipMalloc(&dev, cap) != hipSuccess) return GS_ERR_HIP;
+    out = DevBuffer{dev, cap, device};
     return GS_OK;
 }
 
-// Frees an evicted list once its device has finished the work queued so far
-// (every kernel that reads it was enqueued under the cache lock, before this).
-void free_list(const CachedList &cl, int current_device) {
-    if (cl.device != current_device) (void)hipSetDevice(cl.device);
-    (void)hipDeviceSynchronize();
-    (void)hipFree(cl.dev);
-    if (cl.device != current_device) (void)hipSetDevice(current_device);
+gs_status upload_stream(ListCache &c, int device, hipStream_t *s) {
+    auto it = c.upload_stream.find(device);
+    if (it != c.upload_stream.end()) {
+        *s = it->second;
+        return GS_OK;
+    }
+    if (hipStreamCreateWithFlags(s, hipStreamNonBlocking) != hipSuccess) return GS_ERR_HIP;
+    c.upload_stream.emplace(device, *s);
+    return GS_OK;
+}
+
+gs_status build_list(ListCache &c, int device, int32_t n, const void *const *in,
+                     float *const *out, const int64_t *numel, CachedList &cl) {
+    std::vector<gsk::ChunkDesc> host;
+    gs_status st = make_descriptors(n, in, out, numel, host);
+    if (st != GS_OK) return st;
+    const size_t bytes = host.size() * sizeof(gsk::ChunkDesc);
+    hipStream_t up;
+    st = upload_stream(c, device, &up);
+    if (st != GS_OK) return st;
+    DevBuffer buf;
+    st = take_buffer(c, device, bytes, buf);
+    if (st != GS_OK) return st;
+    if (hipMemcpyAsync(buf.dev, host.data(), bytes, hipMemcpyHostToDevice, up) != hipSuccess ||
+        hipStreamSynchronize(up) != hipSuccess) {
+        c.retired.push_front(Retired{buf, {}});      // idle: reusable at once
+        return GS_ERR_HIP;
+    }
+    cl.buf = buf;
+    cl.nchunks = int64_t(host.size());
+    return GS_OK;
+}
+
+// After a launch that reads the list on `stream`: pin the list when the
+// stream is capturing (or its state cannot be read), else re-record the
+// stream's event.
+void note_use(CachedList &cl, hipStream_t stream) {
+    if (cl.pinned) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        cl.pinned = true;
+        return;
+    }
+    for (StreamUse &u : cl.uses)
+        if (u.stream == stream) {
+            if (hipEventRecord(u.event, stream) != hipSuccess) cl.pinned = true;
+            return;
+        }
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence) !=
+        hipSuccess) {
+        cl.pinned = true;
+        return;
+    }
+    if (hipEventRecord(ev, stream) != hipSuccess) {
+        (void)hipEventDestroy(ev);
+        cl.pinned = true;
+        return;
+    }
+    cl.uses.push_back(StreamUse{stream, ev});
+}
+
+// Evicts least recently used, unpinned lists until one more list of `need`
+// bytes fits (or only pinned lists are left); their buffers are retired.
+// Idle retired buffers beyond kCacheBytes on this device are moved to
+// `to_free` (freed by the caller after the lock is released).
+void make_room(ListCache &c, int device, size_t need, std::vector<void *> &to_free) {
+    auto it = c.lru.end();
+    while (it != c.lru.begin() && (c.map.size() >= kCacheEntries || c.bytes + need > kCacheBytes)) {
+        --it;
+        auto mit = c.map.find(*it);
+        CachedList &old = mit->second.first;
+        if (old.pinned) continue;
+        c.bytes -= old.buf.cap;
+        c.retired.push_front(Retired{old.buf, std::move(old.uses)});
+        c.map.erase(mit);
+        it = c.lru.erase(it);
+    }
+    size_t retired_bytes = 0;
+    for (auto r = c.retired.begin(); r != c.retired.end();) {
+        if (r->buf.device == device) {
+            retired_bytes += r->buf.cap;
+            if (retired_bytes > kCacheBytes && uses_done(r->uses)) {
+                retired_bytes -= r->buf.cap;
+                destroy_uses(r->uses);
+                to_free.push_back(r->buf.dev);
+                r = c.retired.erase(r);
+                continue;
+            }
+        }
+        ++r;
+    }
 }
 
 // Looks up (or builds and caches) the list's descriptors and calls
-// launch(list) with the cache lock held.
+// launch(list) with the cache lock held; then notes the launch's stream.
 template <typename F>
 gs_status with_list(int32_t n, const void *const *in, float *const *out, const int64_t *numel,
-                    F &&launch) {
+                    hipStream_t stream, F &&launch) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return GS_ERR_HIP;
     std::string key = make_key(device, n, in, out, numel);
     ListCache &c = cache();
-    std::lock_guard<std::mutex> lock(c.mu);
-    auto it = c.map.find(key);
-    if (it != c.map.end()) {
-        c.lru.splice(c.lru.begin(), c.lru, it->second.second);
-        return launch(static_cast<const CachedList &>(it->second.first));
+    std::vector<void *> to_free;
+    gs_status st;
+    {
+        std::lock_guard<std::mutex> lock(c.mu);
+        auto it = c.map.find(key);
+        if (it != c.map.end()) {
+            c.lru.splice(c.lru.begin(), c.lru, it->second.second);
+            CachedList &cl = it->second.first;
+            st = launch(static_cast<const CachedList &>(cl));
+            if (st == GS_OK) note_use(cl, stream);
+            return st;
+        }
+        CachedList cl;
+        st = build_list(c, device, n, in, out, numel, cl);
+        if (st != GS_OK) return st;
+        make_room(c, device, cl.buf.cap, to_free);
+        c.lru.push_front(key);
+        auto ins = c.map.emplace(key, std::make_pair(std::move(cl), c.lru.begin())).first;
+        CachedList &added = ins->second.first;
+        c.bytes += added.buf.cap;
+        st = launch(static_cast<const CachedList &>(added));
+        if (st == GS_OK) note_use(added, stream);
     }
-    CachedList cl;
-    const gs_status st = build_list(n, in, out, numel, cl);
-    if (st != GS_OK) return st;
-    cl.device = device;
-    while (!c.lru.empty() && (c.map.size() >= kCacheEntries || c.bytes + cl.bytes > kCacheBytes)) {
-        auto oit = c.map.find(c.lru.back());
-        free_list(oit->second.first, device);
-        c.bytes -= oit->second.first.bytes;
-        c.map.erase(oit);
-        c.lru.pop_back();
-    }
-    c.lru.push_front(key);
-    c.map.emplace(key, std::make_pair(cl, c.lru.begin()));
-    c.bytes += cl.bytes;
-    return launch(static_cast<const CachedList &>(cl));
+    for (void *p : to_free) (void)hipFree(p);   // idle buffers past the retired limit
+    return st;
 }
 
 inline bool bad_enum_fmt(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
@@ -201,6 +339,27 @@ gs_status check_list(int32_t n, const void *const *grads, float *const *outs,
 
 }  // namespace
 
+namespace gsk {
+
+// Argument checks of an fp8_quantize call (everything but the workspace).
+gs_status check_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                         fp8_format fmt, fp8_granularity g, fp8_scale_mode mode,
+                         const uint8_t *codes, const float *scales, const int32_t *nonfinite) {
+    if (x_dtype != GS_BF16 && x_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (bad_enum_fmt(fmt) || bad_enum_gran(g)) return GS_ERR_ARG;
+    if (mode != FP8_SCALE_FROM_AMAX && mode != FP8_SCALE_GIVEN) return GS_ERR_ARG;
+    const gs_status st = check_shape(rows, cols, g);
+    if (st != GS_OK) return st;
+    if (rows * cols > 0 && (!x || !codes)) return GS_ERR_NULL;
+    if (num_scales(rows, cols, g) > 0 && !scales) return GS_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(scales, 4) ||
+        misaligned(nonfinite, 4))
+        return GS_ERR_ALIGN;
+    return GS_OK;
+}
+
+}  // namespace gsk
+
 extern "C" {
 
 gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *outs,
@@ -214,10 +373,10 @@ gs_status gs_unscale_check(int32_t n, const void *const *grads, float *const *ou
     const gs_status vs = check_list(n, grads, outs, numels, &total);
     if (vs != GS_OK) return vs;
     if (total == 0) return GS_OK;
-    return with_list(n, grads, outs, numels, [&](const CachedList &cl) {
-        return from_hip(gsk::launch_unscale_check(static_cast<const gsk::ChunkDesc *>(cl.dev),
-                                                  cl.nchunks, scale, found_inf,
-                                                  static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return with_list(n, grads, outs, numels, s, [&](const CachedList &cl) {
+        return from_hip(gsk::launch_unscale_check(static_cast<const gsk::ChunkDesc *>(cl.buf.dev),
+                                                  cl.nchunks, scale, found_inf, s));
     });
 }
 
@@ -266,13 +425,14 @@ gs_status gs_unscale_check_sumsq(int32_t n, const void *const *grads, float *con
     if (!workspace || workspace_bytes < gs_unscale_check_sumsq_workspace_size(n, numels))
         return GS_ERR_WORKSPACE;
     if (misaligned(workspace, 16)) return GS_ERR_ALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     auto launch = [&](const CachedList &cl) {
         return from_hip(gsk::launch_unscale_check_sumsq(
-            static_cast<const gsk::ChunkDesc *>(cl.dev), cl.nchunks, scale, found_inf, sumsq,
-            norm_sq, workspace, static_cast<hipStream_t>(stream)));
+            static_cast<const gsk::ChunkDesc *>(cl.buf.dev), cl.nchunks, scale, found_inf, sumsq,
+            norm_sq, workspace, s));
     };
     if (total == 0) return launch(CachedList{});   // still folds the total into norm_sq
-    return with_list(n, grads, outs, numels, launch);
+    return with_list(n, grads, outs, numels, s, launch);
 }
 
 gs_status gs_update_scale(float *scale, int32_t *growth_tracker, int32_t *found_inf,
@@ -321,17 +481,9 @@ gs_status fp8_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t co
                        fp8_format fmt, fp8_granularity g, fp8_scale_mode mode, uint8_t *codes,
                        float *scales, int32_t *nonfinite, void *workspace,
                        size_t workspace_bytes, void *stream) {
-    if (x_dtype != GS_BF16 && x_dtype != GS_F32) return GS_ERR_DTYPE;
-    if (bad_enum_fmt(fmt) || bad_enum_gran(g)) return GS_ERR_ARG;
-    if (mode != FP8_SCALE_FROM_AMAX && mode != FP8_SCALE_GIVEN) return GS_ERR_ARG;
-    gs_status st = check_shape(rows, cols, g);
+    const gs_status st = gsk::check_quantize(x, x_dtype, rows, cols, fmt, g, mode, codes,
+                                             scales, nonfinite);
     if (st != GS_OK) return st;
-    const int64_t n = rows * cols;
-    if (n > 0 && (!x || !codes)) return GS_ERR_NULL;
-    if (num_scales(rows, cols, g) > 0 && !scales) return GS_ERR_NULL;
-    if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(scales, 4) ||
-        misaligned(nonfinite, 4))
-        return GS_ERR_ALIGN;
     const bool need_ws = (g == FP8_PER_TENSOR && mode == FP8_SCALE_FROM_AMAX);
     if (need_ws) {
         if (!workspace || workspace_bytes < fp8_quantize_workspace_size(rows, cols, g))

@@ -80,6 +80,12 @@ hipError_t launch_update_scale(float *scale, int32_t *tracker, int32_t *found_in
 // ---------------------------------------------------------------- FP8
 constexpr int kPartialSlots = 8192;   // per-tensor amax partials (workspace words)
 
+// Argument checks of an fp8_quantize call, everything but the workspace
+// (defined in api.hip).
+gs_status check_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                         fp8_format fmt, fp8_granularity g, fp8_scale_mode mode,
+                         const uint8_t *codes, const float *scales, const int32_t *nonfinite);
+
 hipError_t launch_quantize(const void *x, gs_dtype dt, int64_t rows, int64_t cols, int fmt,
                            int gran, int mode, uint8_t *codes, float *scales,
                            int32_t *nonfinite, uint32_t *partials, hipStream_t stream);

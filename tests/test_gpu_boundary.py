@@ -307,3 +307,138 @@ def test_extended_step_captured_in_a_hip_graph(dev):
         assert np.array_equal(_bits(d_mx), oracle.dequantize_mx(rc_mx, gs.FP8_E4M3, rs_mx).view(np.uint32)), r
     # closed form: replays 1-2 clean (tracker 2), 3 spends the budget, 4 lowers S, 5-6 clean
     assert (float(RS.S), RS.skips.value, RS.tracker.value) == (32768.0, 2, 2)
+
+
+def _small_lists(rng, dev, count, seed_sizes=(2500, 301, 9000)):
+    """`count` distinct gradient lists of similar sizes (so their descriptor
+    buffers are interchangeable), as (host, device grads, device outputs)."""
+    lists = []
+    for k in range(count):
+        sizes = [int(n + (k * 37) % 97) for n in seed_sizes]
+        host = [_random_f16(rng, n) for n in sizes]
+        lists.append((host, [_to_dev(h, dev) for h in host],
+                      [torch.empty(n, dtype=torch.float32, device=dev) for n in sizes]))
+    return lists
+
+
+def test_list_captured_in_a_graph_survives_eviction(dev):
+    """A list used while its stream captures a graph stays cached: after 80
+    other lists have gone through the 64-list cache (evicting lists and
+    reusing their retired descriptor buffers), replaying the graph still
+    reads its own descriptors, and every replay and every eager call matches
+    the oracle.  Every tensor stays alive to the end, so a wrong reuse could
+    only misdirect writes into live buffers."""
+    rng = np.random.default_rng(83)
+    (host, g, o), = _small_lists(rng, dev, 1, (4000, 123, 30000))
+    S = torch.tensor([512.0], dtype=torch.float32, device=dev)
+    f = torch.zeros(1, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gs.gs_unscale_check(g, o, S, f)          # first call: builds and caches the list
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gs.gs_unscale_check(g, o, S, f)
+    torch.cuda.synchronize()
+    others = _small_lists(rng, dev, 80)
+    ref, rf = oracle.unscale_check(host, 512.0)
+    for rnd in range(3):
+        for k, (oh, og, oo) in enumerate(others):
+            of = torch.zeros(1, dtype=torch.int32, device=dev)
+            gs.gs_unscale_check(og, oo, S, of)
+            if k % 9 == rnd:
+                oref, orf = oracle.unscale_check(oh, 512.0)
+                torch.cuda.synchronize()
+                for out, r in zip(oo, oref):
+                    assert np.array_equal(_bits(out), r.view(np.uint32)), (rnd, k)
+                assert int(of.item()) == orf
+        for out in o:
+            out.fill_(-3.0)
+        f.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for out, r in zip(o, ref):
+            assert np.array_equal(_bits(out), r.view(np.uint32)), rnd
+        assert int(f.item()) == rf
+
+
+def test_evictions_while_another_thread_captures(dev):
+    """Thread B pushes distinct gradient lists through the cache on its own
+    stream (evictions, and retired descriptor buffers reused once the events
+    of their last launches have completed) while thread A, on its own
+    stream, repeatedly captures an unscale + update step in a HIP graph
+    (thread-local capture mode, so that B may allocate and upload meanwhile)
+    and replays each graph three times with eager work between the replays.
+    Every result of both threads matches the oracle.  All tensors are made
+    before the threads start and stay alive to the end."""
+    rng = np.random.default_rng(84)
+    (hA, gA, oA), = _small_lists(rng, dev, 1, (6000, 50, 20000))
+    hA[1][7] = 0x7C00                           # an Inf: every replay overflows and skips
+    gA[1][7:8] = _to_dev(np.array([0x7C00], np.uint16), dev)
+    SA = torch.tensor([2.0 ** 20], dtype=torch.float32, device=dev)
+    trA = torch.zeros(1, dtype=torch.int32, device=dev)
+    fA = torch.zeros(1, dtype=torch.int32, device=dev)
+    listsB = _small_lists(rng, dev, 160)
+    SB = torch.tensor([128.0], dtype=torch.float32, device=dev)
+    fB = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in listsB]
+    torch.cuda.synchronize()
+    errors, a_done, b_started = [], threading.Event(), threading.Event()
+
+    def thread_a():
+        try:
+            sA = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(sA):
+                gs.gs_unscale_check(gA, oA, SA, fA)     # caches the list
+                sA.synchronize()
+                fA.zero_()
+                b_started.wait(30)
+                R = oracle.ScalerState(2.0 ** 20)
+                for cap in range(6):
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph, stream=sA, capture_error_mode="thread_local"):
+                        gs.gs_unscale_check(gA, oA, SA, fA)
+                        gs.gs_update_scale(SA, trA, fA, 2.0, 0.5, 3)
+                    for r in range(3):
+                        for out in oA:
+                            out.fill_(-2.0)
+                        graph.replay()
+                        ref, rf = oracle.unscale_check(hA, float(R.S))
+                        R.found_inf.value = rf
+                        oracle.update_scale(R, 2.0, 0.5, 3)
+                        sA.synchronize()
+                        for out, rr in zip(oA, ref):
+                            assert np.array_equal(_bits(out), rr.view(np.uint32)), (cap, r)
+                        assert float(SA.item()) == float(R.S), (cap, r)
+        except Exception as e:          # noqa: BLE001 -- reported below
+            errors.append(("A", repr(e)))
+        finally:
+            a_done.set()
+
+    def thread_b():
+        try:
+            sB = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(sB):
+                k = 0
+                while k < len(listsB) and (k < 100 or not a_done.is_set()):
+                    host, g, o = listsB[k]
+                    gs.gs_unscale_check(g, o, SB, fB[k])
+                    b_started.set()
+                    ref, rf = oracle.unscale_check(host, 128.0)
+                    sB.synchronize()
+                    for out, rr in zip(o, ref):
+                        assert np.array_equal(_bits(out), rr.view(np.uint32)), k
+                    assert int(fB[k].item()) == rf, k
+                    k += 1
+        except Exception as e:          # noqa: BLE001 -- reported below
+            errors.append(("B", repr(e)))
+        finally:
+            b_started.set()
+
+    ta, tb = threading.Thread(target=thread_a), threading.Thread(target=thread_b)
+    ta.start()
+    tb.start()
+    ta.join()
+    tb.join()
+    assert not errors, errors

@@ -1,16 +1,25 @@
 """GPU parity at the full benchmark sizes, in the launch configuration the
-benchmark times: sampled outputs checked one by one against the oracle, plus
-properties that hold at any size.
+benchmark times, against the oracle on every element: the outputs are copied
+to the host and checked in row bands (or per tensor) on a pool of host
+threads, each band by the oracle's own functions.
 
 Workloads (seeded, synthetic; see synth/):
   * Llama-3-8B-shaped FP16 gradient set, 291 tensors / 8,030,261,248
-    elements, S = 2^15, 10 steps with an Inf in lm_head at step 2;
+    elements, S = 2^15, 10 steps with an Inf in lm_head at step 2: every
+    output of steps 1-3 against the oracle (the clean step at 2^15, the
+    Inf step, the clean step at 2^14); steps 4-10 repeat step 3's inputs and
+    scale, so their outputs are compared with step 3's on the device; the
+    flag and S / tracker / skips at every step;
   * DeepSeek-V3-shaped BF16 activations 16384x7168 (1x128) and weights
-    7168x18432 (128x128), E4M3;
+    7168x18432 (128x128), E4M3: codes, scales, FP32 dequantize;
   * 8192x8192 per-tensor E4M3 (0.1% x1000 outliers) and E5M2 (Laplace);
-  * four 16384x32768 special-value tensors, every granularity, both
-    formats, both scale modes.
+  * four 16384x32768 special-value tensors: every granularity, both
+    formats, scales from the amax and given scales of 1, with dequantize;
+  * 1x32 / MX blocks and matrices past 2^32 elements: sampled blocks.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -22,6 +31,14 @@ import synth
 pytestmark = pytest.mark.gpu
 
 PT, B1, B128 = gs.FP8_PER_TENSOR, gs.FP8_BLOCK_1x128, gs.FP8_BLOCK_128x128
+
+# host threads for the oracle (its C calls release the GIL): the job's share
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+_POOL = ThreadPoolExecutor(_THREADS)
+
+
+def _pmap(fn, items):
+    return list(_POOL.map(fn, items))
 
 
 @pytest.fixture(scope="module")
@@ -48,53 +65,6 @@ def test_generators_identical_on_cpu_and_gpu(dev):
     g = synth.llama3_8b_gradset()
     for t in (0, 5, 290):
         assert torch.equal(g.gen(t, idx), g.gen(t, idx.to(dev)).cpu())
-
-
-def test_llama3_8b_gradset_10_steps(dev):
-    g = synth.llama3_8b_gradset()
-    grads = [g.full(t, dev) for t in range(len(g.tensors))]
-    outs = [torch.empty(sp.numel, dtype=torch.float32, device=dev) for sp in g.tensors]
-    S = torch.tensor([g.scale], dtype=torch.float32, device=dev)
-    tracker = torch.zeros(1, dtype=torch.int32, device=dev)
-    found = torch.zeros(1, dtype=torch.int32, device=dev)
-    skips = torch.zeros(1, dtype=torch.int64, device=dev)
-    R = oracle.ScalerState(g.scale)
-    rng = np.random.default_rng(44)
-    inj_t, inj_i, inj_bits = g.injections[2][0]
-    inj_orig = int(g.gen(inj_t, torch.tensor([inj_i]))[0])
-    for step in range(1, g.steps + 1):
-        if step == 2:
-            grads[inj_t][inj_i:inj_i + 1].fill_(float("inf"))
-        gs.gs_unscale_check(grads, outs, S, found)
-        # samples: random elements of every tensor, both ends of each, the injection
-        S_before = float(R.S)
-        for t, sp in enumerate(g.tensors):
-            n = sp.numel
-            k = max(8, min(4096, n // 100000))
-            idx = np.unique(np.concatenate([rng.integers(0, n, k), np.arange(min(8, n)),
-                                            np.arange(max(0, n - 8), n)]))
-            if t == inj_t:
-                idx = np.unique(np.append(idx, inj_i))
-            ti = torch.from_numpy(idx)
-            bits = g.gen(t, ti).numpy().astype(np.uint16)
-            if step == 2 and t == inj_t:
-                bits[np.searchsorted(idx, inj_i)] = inj_bits
-            ref, _ = oracle.unscale_check([bits], S_before)
-            got = outs[t][ti.to(dev)]
-            assert np.array_equal(_u32(got), ref[0].view(np.uint32)), (step, t)
-        # property over every element: non-finite outputs exactly where injected
-        finite = torch.stack([torch.isfinite(o).all() for o in outs]).all().item()
-        assert finite == (step != 2)
-        assert int(found.item()) == (1 if step == 2 else 0)
-        R.found_inf.value = int(found.item())
-        gs.gs_update_scale(S, tracker, found, 2.0, 0.5, 2000, skips)
-        oracle.update_scale(R, 2.0, 0.5, 2000)
-        torch.cuda.synchronize()
-        assert (float(S.item()), int(tracker.item()), int(skips.item())) == \
-            (float(R.S), R.tracker.value, R.skips.value)
-        if step == 2:
-            grads[inj_t][inj_i:inj_i + 1].fill_(float(np.uint16(inj_orig).view(np.float16)))
-    assert (float(R.S), R.tracker.value, R.skips.value) == (2.0 ** 14, 8, 1)
 
 
 def _check_blocks(x_spec, codes, scales, deq, gran, fmt, rng, nsample):
@@ -136,24 +106,6 @@ def _check_blocks(x_spec, codes, scales, deq, gran, fmt, rng, nsample):
     return checked
 
 
-def test_deepseek_v3_block_shapes(dev):
-    rng = np.random.default_rng(33)
-    for sp in synth.deepseek_v3_blocks():
-        x = sp.full(dev)
-        nf = torch.zeros(1, dtype=torch.int32, device=dev)
-        codes, scales = gs.fp8_quantize(x, sp.fmt, sp.gran, nonfinite=nf)
-        deq = gs.fp8_dequantize(codes, sp.fmt, sp.gran, scales)
-        torch.cuda.synchronize()
-        # properties at full size: finite positive scales, no NaN codes, no flag
-        assert torch.isfinite(scales).all() and (scales > 0).all()
-        assert not ((codes & 0x7F) == 0x7F).any()
-        assert int(nf.item()) == 0
-        assert tuple(scales.shape) == gs.scale_shape(sp.rows, sp.cols, sp.gran)
-        n = _check_blocks(sp, codes, scales, deq, sp.gran, sp.fmt, rng,
-                          3000 if sp.gran == B1 else 40)
-        assert n >= (2500 if sp.gran == B1 else 35)
-
-
 def test_per_tensor_at_scale_full_compare(dev):
     """8192x8192 per-tensor: the whole tensor against the oracle (the input
     bits are the generator's, produced on the GPU and checked identical to
@@ -169,60 +121,6 @@ def test_per_tensor_at_scale_full_compare(dev):
         assert np.array_equal(codes.cpu().numpy(), rc), sp.name
         rd = oracle.dequantize(rc, sp.fmt, PT, rs)
         assert np.array_equal(_u32(deq), rd.reshape(-1).view(np.uint32)), sp.name
-
-
-def test_special_values_4gib_all_modes(dev):
-    rng = np.random.default_rng(55)
-    blocks_checked = elems_checked = 0
-    for sp in synth.special_values_4gib():
-        x = sp.full(dev)
-        n = sp.rows * sp.cols
-        xf = x.float()
-        finite = torch.isfinite(xf)
-        expect_nf = int((~finite).any().item())
-        amax = torch.where(finite, xf.abs(), torch.zeros_like(xf)).max().item()
-        del xf, finite
-        samp = np.unique(np.concatenate([rng.integers(0, n, 200000), np.arange(256),
-                                         np.arange(n - 256, n)]))
-        ts = torch.from_numpy(samp)
-        xs = sp.gen(ts).numpy().astype(np.uint16)
-        xs_f32 = (xs.astype(np.uint32) << 16).view(np.float32)
-        for fmt in (gs.FP8_E4M3, gs.FP8_E5M2):
-            for gran in (PT, B1, B128):
-                for mode in (gs.FP8_SCALE_FROM_AMAX, gs.FP8_SCALE_GIVEN):
-                    nf = torch.zeros(1, dtype=torch.int32, device=dev)
-                    sc = None
-                    if mode == gs.FP8_SCALE_GIVEN:
-                        sc = torch.ones(gs.scale_shape(sp.rows, sp.cols, gran),
-                                        dtype=torch.float32, device=dev)
-                    codes, scales = gs.fp8_quantize(x, fmt, gran, mode, scales=sc, nonfinite=nf)
-                    deq = gs.fp8_dequantize(codes, fmt, gran, scales)
-                    torch.cuda.synchronize()
-                    assert int(nf.item()) == expect_nf
-                    tag = (sp.name, fmt, gran, mode)
-                    if mode == gs.FP8_SCALE_GIVEN:
-                        ref = oracle.cast(xs_f32, 1.0, fmt)
-                        got = codes.view(-1)[ts.to(dev)].cpu().numpy()
-                        assert np.array_equal(got, ref), tag
-                        rd = oracle.dequantize(ref.reshape(1, -1), fmt, PT, np.float32([1.0]))
-                        assert np.array_equal(_u32(deq.view(-1)[ts.to(dev)]),
-                                              rd.reshape(-1).view(np.uint32)), tag
-                        elems_checked += got.size
-                    elif gran == PT:
-                        s_ref = oracle.scale_from_amax(amax, fmt)
-                        assert _u32(scales)[0] == np.float32(s_ref).view(np.uint32), tag
-                        ref = oracle.cast(xs_f32, float(s_ref), fmt)
-                        got = codes.view(-1)[ts.to(dev)].cpu().numpy()
-                        assert np.array_equal(got, ref), tag
-                        elems_checked += got.size
-                    else:
-                        blocks_checked += _check_blocks(sp, codes, scales, deq, gran, fmt, rng,
-                                                        400 if gran == B1 else 6)
-                    del codes, scales, deq
-        del x
-        torch.cuda.empty_cache()
-    print("special values: %d blocks and %d sampled elements checked" % (blocks_checked, elems_checked))
-    assert blocks_checked >= 4 * 2 * (380 + 6) and elems_checked >= 4 * 2 * 4 * 190000
 
 
 def _check_row32_blocks(x_spec, codes, scales, deq, mx, fmt, rng, nsample):
@@ -339,3 +237,187 @@ def test_tensors_above_2_32_elements(dev):
     deq = gs.fp8_dequantize_mx(codes, gs.FP8_E5M2, sc)
     torch.cuda.synchronize()
     assert _check_row32_blocks(sp, codes, sc, deq, True, gs.FP8_E5M2, rng, 600) >= 500
+
+
+# ---------------------------------------------------------------- whole tensors
+def _bands_equal(got, ref, what, where):
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)[:4]
+        raise AssertionError("%s differ at %s (band %s): gpu %s oracle %s" % (
+            what, bad.tolist(), where, [hex(int(got[tuple(b)])) for b in bad],
+            [hex(int(ref[tuple(b)])) for b in bad]))
+
+
+def _check_rows(xh, ch, sh, dh, fmt, gran, mode=gs.FP8_SCALE_FROM_AMAX, given=None):
+    """Every element of a quantize + dequantize against the oracle, in bands
+    of 128 rows (whole blocks at every granularity).  xh: BF16 bits
+    [rows, cols]; ch codes; sh scales as uint32 bits in the block layout
+    ([rows, cols/128], [rows/128, cols/128], or [1]); dh dequantized FP32 as
+    uint32 bits.  Per-tensor bands cast with `given`, the scale the oracle
+    derived from the whole tensor (or the given scale).  Returns the
+    oracle's nonfinite flag."""
+    rows = xh.shape[0]
+
+    def band(r0):
+        sl = slice(r0, min(r0 + 128, rows))
+        if gran == PT:
+            sc = np.float32([given])
+            rc, _, rnf = oracle.quantize(xh[sl], fmt, PT, gs.FP8_SCALE_GIVEN, sc)
+            rs = sc
+        elif mode == gs.FP8_SCALE_GIVEN:
+            rs = np.full(oracle.n_scales(sl.stop - r0, xh.shape[1], gran), given, np.float32)
+            rc, _, rnf = oracle.quantize(xh[sl], fmt, gran, mode, rs)
+        else:
+            rc, rs, rnf = oracle.quantize(xh[sl], fmt, gran)
+            got_s = sh[sl] if gran == B1 else sh[r0 // 128]
+            _bands_equal(got_s.reshape(-1), rs.reshape(-1).view(np.uint32), "scales", r0)
+        _bands_equal(ch[sl], rc, "codes", r0)
+        rd = oracle.dequantize(rc, fmt, gran if gran != PT else PT, rs)
+        _bands_equal(dh[sl], rd.view(np.uint32), "dequantized values", r0)
+        return rnf
+
+    return max(_pmap(band, range(0, rows, 128)))
+
+
+def _oracle_tensor_amax(xh):
+    cols = xh.shape[1]
+    return max(_pmap(lambda r0: float(oracle.block_amax(xh, r0, min(128, xh.shape[0] - r0), 0, cols)),
+                     range(0, xh.shape[0], 128)))
+
+
+@pytest.mark.timeout(900)
+def test_deepseek_v3_block_shapes_every_element(dev):
+    for sp in synth.deepseek_v3_blocks():
+        print("deepseek-v3 %s %dx%d gran %d" % (sp.name, sp.rows, sp.cols, sp.gran), flush=True)
+        x = sp.full(dev)
+        nf = torch.zeros(1, dtype=torch.int32, device=dev)
+        codes, scales = gs.fp8_quantize(x, sp.fmt, sp.gran, nonfinite=nf)
+        deq = gs.fp8_dequantize(codes, sp.fmt, sp.gran, scales)
+        torch.cuda.synchronize()
+        assert tuple(scales.shape) == gs.scale_shape(sp.rows, sp.cols, sp.gran)
+        xh = _u16(x).reshape(sp.rows, sp.cols)
+        ch = codes.cpu().numpy()
+        sh = scales.cpu().numpy().view(np.uint32)
+        dh = deq.cpu().numpy().view(np.uint32)
+        rnf = _check_rows(xh, ch, sh, dh, sp.fmt, sp.gran)
+        assert int(nf.item()) == rnf == 0
+
+
+@pytest.mark.timeout(900)
+def test_llama3_8b_gradset_every_element(dev):
+    g = synth.llama3_8b_gradset()
+    grads = [g.full(t, dev) for t in range(len(g.tensors))]
+    outs = [torch.empty(sp.numel, dtype=torch.float32, device=dev) for sp in g.tensors]
+    S = torch.tensor([g.scale], dtype=torch.float32, device=dev)
+    tracker = torch.zeros(1, dtype=torch.int32, device=dev)
+    found = torch.zeros(1, dtype=torch.int32, device=dev)
+    skips = torch.zeros(1, dtype=torch.int64, device=dev)
+    R = oracle.ScalerState(g.scale)
+    inj_t, inj_i, inj_bits = g.injections[2][0]
+    inj_orig = int(g.gen(inj_t, torch.tensor([inj_i]))[0])
+    host_in = [_u16(t) for t in grads]              # the inputs, copied once
+    piece = 1 << 24
+    snapshot = None
+    for step in range(1, g.steps + 1):
+        if step == 2:
+            grads[inj_t][inj_i:inj_i + 1].fill_(float("inf"))
+            host_in[inj_t][inj_i] = inj_bits
+        gs.gs_unscale_check(grads, outs, S, found)
+        torch.cuda.synchronize()
+        S_before = float(R.S)
+        if step <= 3:
+            print("llama3-8b step %d: every element, S = %g" % (step, S_before), flush=True)
+            pending = []
+            for t in range(len(g.tensors)):
+                out_h = _u32(outs[t])
+                xin = host_in[t]
+
+                def check(lo, xin=xin, out_h=out_h, t=t):
+                    ref, rf = oracle.unscale_check([xin[lo:lo + piece]], S_before)
+                    _bands_equal(out_h[lo:lo + piece], ref[0].view(np.uint32),
+                                 "step %d tensor %d outputs" % (step, t), lo)
+                    return rf
+                pending.append(_POOL.map(check, range(0, xin.size, piece)))
+                if len(pending) > 8:                  # bound the host copies in flight
+                    pending = [list(p) for p in pending]
+            rf = max(max(p) for p in pending)
+            if step == 3:
+                snapshot = [o.clone() for o in outs]
+                rf3 = rf
+        else:
+            # same inputs and scale as step 3: the same outputs on every element
+            for t, (o, s0) in enumerate(zip(outs, snapshot)):
+                assert torch.equal(o.view(torch.int32), s0.view(torch.int32)), (step, t)
+            rf = rf3
+        assert int(found.item()) == rf == (1 if step == 2 else 0), step
+        R.found_inf.value = rf
+        gs.gs_update_scale(S, tracker, found, 2.0, 0.5, 2000, skips)
+        oracle.update_scale(R, 2.0, 0.5, 2000)
+        torch.cuda.synchronize()
+        assert (float(S.item()), int(tracker.item()), int(skips.item())) == \
+            (float(R.S), R.tracker.value, R.skips.value), step
+        if step == 2:
+            grads[inj_t][inj_i:inj_i + 1].fill_(float(np.uint16(inj_orig).view(np.float16)))
+            host_in[inj_t][inj_i] = inj_orig
+    assert (float(R.S), R.tracker.value, R.skips.value) == (2.0 ** 14, 8, 1)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mix", "anchored", "saturation", "random"])
+def test_special_values_4gib_every_element(dev, name):
+    """One 16384x32768 special-value tensor: quantize at per-tensor, 1x128
+    and 128x128 with scales from the amax, and with given scales of 1, in
+    both formats, each followed by the FP32 dequantize; every code, scale
+    and dequantized value against the oracle, and the nonfinite flag.
+    Per-tensor: the oracle's largest finite |x| over the whole tensor (the
+    maximum of its row bands' maxima) gives the scale that every band is
+    then cast with, the steps of the oracle's per-tensor quantize.  Given
+    scales of 1: the three granularities give identical codes (compared on
+    the device), and one of them is compared with the oracle."""
+    sp = [s for s in synth.special_values_4gib() if s.name == name][0]
+    R, C = sp.rows, sp.cols
+    x = sp.full(dev)
+    xh = _u16(x).reshape(R, C)
+    amax = _oracle_tensor_amax(xh)
+    flags = set()
+    for fmt in (gs.FP8_E4M3, gs.FP8_E5M2):
+        for gran in (B1, B128, PT):
+            print("special values %s fmt %d gran %d amax mode" % (name, fmt, gran), flush=True)
+            nf = torch.zeros(1, dtype=torch.int32, device=dev)
+            codes, scales = gs.fp8_quantize(x, fmt, gran, nonfinite=nf)
+            deq = gs.fp8_dequantize(codes, fmt, gran, scales)
+            torch.cuda.synchronize()
+            ch, sh = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint32)
+            del codes
+            dh = deq.cpu().numpy().view(np.uint32)
+            del deq
+            s_ref = None
+            if gran == PT:
+                s_ref = np.float32(oracle.scale_from_amax(amax, fmt))
+                assert sh.reshape(-1)[0] == s_ref.view(np.uint32), (name, fmt)
+            rnf = _check_rows(xh, ch, sh, dh, fmt, gran, given=s_ref)
+            assert int(nf.item()) == rnf, (name, fmt, gran)
+            flags.add(rnf)
+            del ch, dh
+        print("special values %s fmt %d given scales 1" % (name, fmt), flush=True)
+        first = None
+        for gran in (PT, B1, B128):
+            sc = torch.ones(gs.scale_shape(R, C, gran), dtype=torch.float32, device=dev)
+            nf = torch.zeros(1, dtype=torch.int32, device=dev)
+            codes, _ = gs.fp8_quantize(x, fmt, gran, gs.FP8_SCALE_GIVEN, scales=sc, nonfinite=nf)
+            deq = gs.fp8_dequantize(codes, fmt, gran, sc)
+            torch.cuda.synchronize()
+            flags.add(int(nf.item()))
+            if first is None:
+                first = (codes, deq)
+            else:
+                assert torch.equal(codes, first[0]), (name, fmt, gran)
+                assert torch.equal(deq.view(torch.int32), first[1].view(torch.int32)), (name, fmt, gran)
+                del codes, deq
+        ch = first[0].cpu().numpy()
+        dh = first[1].cpu().numpy().view(np.uint32)
+        del first
+        torch.cuda.empty_cache()
+        flags.add(_check_rows(xh, ch, None, dh, fmt, PT, gs.FP8_SCALE_GIVEN, given=1.0))
+        del ch, dh
+    assert len(flags) == 1, flags                   # every mode saw the same inputs

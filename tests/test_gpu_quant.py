@@ -248,3 +248,45 @@ def test_every_fp32_value_given_scale_one(fmt, dev):
             bad = np.flatnonzero(got != ref)[:5]
             raise AssertionError("fp32 patterns %s: gpu %s oracle %s" % (
                 [hex(lo + int(i)) for i in bad], got[bad].tolist(), ref[bad].tolist()))
+
+
+def _fp32_midpoint_matrix(rng, rows, cols, fmt, br, bc):
+    """FP32 [rows, cols] whose br x bc blocks each hold one +-A (a random
+    non-power-of-two amax, exponents -40..40) and elsewhere values within
+    +-8 ulps of x = fl32(m * s) for random midpoints m between adjacent FP8
+    values, with s = fl32(max(A, fl32(1e-12)) / MAX) that block's scale, so
+    that the quotients x / s straddle the FP8 rounding boundaries."""
+    vals = np.unique(np.abs(oracle.fp8_decode_table(fmt)[np.isfinite(oracle.fp8_decode_table(fmt))]))
+    mids = (vals[:-1] + vals[1:]) / 2
+    nbr, nbc = rows // br, cols // bc
+    mant = rng.integers(1, 1 << 23, size=(nbr, nbc)).astype(np.uint32)
+    expo = rng.integers(127 - 40, 127 + 41, size=(nbr, nbc)).astype(np.uint32)
+    A = ((expo << 23) | mant).view(np.float32)
+    s = np.maximum(A, np.float32(1e-12)) / np.float32(oracle.FMT_MAX[fmt])
+    s_full = np.repeat(np.repeat(s, br, 0), bc, 1)
+    A_full = np.repeat(np.repeat(A, br, 0), bc, 1)
+    m = mids[rng.integers(0, mids.size, size=(rows, cols))]
+    x0 = (m * s_full.astype(np.float64)).astype(np.float32)
+    x = (x0.view(np.uint32).astype(np.int64) + rng.integers(-8, 9, size=(rows, cols)))
+    x = np.minimum(x.astype(np.uint32).view(np.float32), A_full)
+    x = np.where(rng.integers(0, 2, size=(rows, cols)) == 1, -x, x).astype(np.float32)
+    for bi in range(nbr):                         # one +-A per block: its amax
+        for bj in range(nbc):
+            r, c = bi * br + rng.integers(0, br), bj * bc + rng.integers(0, bc)
+            x[r, c] = A[bi, bj] if rng.integers(0, 2) else -A[bi, bj]
+    return x
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_fp32_midpoints_with_non_power_of_two_scales(fmt, dev):
+    """FP32 input in amax mode at every granularity: quotients within +-8
+    ulps of FP8 midpoints under non-power-of-two block scales, where a
+    division that is off in the last bit would change the code; codes,
+    scales and dequantized values against the oracle."""
+    rng = np.random.default_rng(2900 + fmt)
+    for gran, (rows, cols), (br, bc) in ((B1, (512, 1024), (1, 128)),
+                                         (B128, (512, 1024), (128, 128)),
+                                         (B32, (256, 1024), (1, 32)),
+                                         (PT, (512, 1024), (512, 1024))):
+        x = _fp32_midpoint_matrix(rng, rows, cols, fmt, br, bc)
+        _check(x, fmt, gran, gs.FP8_SCALE_FROM_AMAX, dev)

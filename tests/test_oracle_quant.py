@@ -24,29 +24,46 @@ def _floats(s):
     return [float(v) for v in s.split(",")]
 
 
-# ---- the page's listing, run by torch CPU on FP32 (codes instead of values)
+# ---- the page's per-block rule, block by block with torch CPU primitives
+def _blocks(shape, gran):
+    """(row slice, column slice) of every block, in the row-major order of
+    the scale layout."""
+    R, C = shape
+    br, bc = BLOCK[gran] or (R, C)
+    return [(slice(r0, r0 + br), slice(c0, c0 + bc))
+            for r0 in range(0, R, br) for c0 in range(0, C, bc)]
+
+
 def _listing_codes_and_scales(x: torch.Tensor, fmt: int, gran: int):
-    MAX = torch.finfo(TORCH_FP8[fmt]).max
-    if gran == PT:
-        s = x.abs().max() / MAX
-        codes = (x / s).clamp(-MAX, MAX).to(TORCH_FP8[fmt])
-        return codes.view(torch.uint8).numpy(), s.reshape(1).numpy()
-    rows, cols = BLOCK[gran]
-    R, C = x.shape
-    b = x.reshape(R // rows, rows, C // cols, cols)
-    s = b.abs().amax(dim=(1, 3), keepdim=True).clamp(min=1e-12) / MAX
-    codes = (b / s).clamp(-MAX, MAX).to(TORCH_FP8[fmt]).reshape(R, C)
-    return codes.view(torch.uint8).numpy(), s.reshape(-1).numpy()
+    """For each block: its largest |x| (the 1e-12 floor applies to blocks;
+    the page's per-tensor function has none, and these inputs never need
+    it), the FP32 scale amax / MAX, then each element divided by the scale,
+    clamped to [-MAX, MAX] and cast by torch to the float8 type (round to
+    nearest even).  Returns the codes as bytes and the scales in block
+    order."""
+    fp8 = TORCH_FP8[fmt]
+    MAX = float(torch.finfo(fp8).max)
+    codes = torch.empty(x.shape, dtype=torch.uint8)
+    scales = []
+    for rs, cs in _blocks(x.shape, gran):
+        block = x[rs, cs]
+        amax = block.abs().max()
+        if gran != PT:
+            amax = torch.clamp(amax, min=1e-12)
+        s = amax / MAX
+        codes[rs, cs] = torch.clamp(block / s, -MAX, MAX).to(fp8).view(torch.uint8)
+        scales.append(s)
+    return codes.numpy(), torch.stack(scales).numpy()
 
 
 def _listing_dequant(codes: np.ndarray, s: np.ndarray, fmt: int, gran: int):
+    """Each block's codes decoded by torch (float8 to float32) times its
+    scale."""
     q = torch.from_numpy(codes).view(TORCH_FP8[fmt]).float()
-    R, C = q.shape
-    if gran == PT:
-        return (q * torch.from_numpy(s)[0]).numpy()
-    rows, cols = BLOCK[gran]
-    st = torch.from_numpy(s).reshape(R // rows, 1, C // cols, 1)
-    return (q.reshape(R // rows, rows, C // cols, cols) * st).reshape(R, C).numpy()
+    out = torch.empty(q.shape, dtype=torch.float32)
+    for k, (rs, cs) in enumerate(_blocks(q.shape, gran)):
+        out[rs, cs] = q[rs, cs] * float(s[k])
+    return out.numpy()
 
 
 def _bf16_bits(x: torch.Tensor) -> np.ndarray:
