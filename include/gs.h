@@ -295,6 +295,32 @@ gs_status fp8_quantize(const void *x, gs_dtype x_dtype, int64_t rows, int64_t co
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fp8_quantize_no_workspace -- fp8_quantize for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments minus the workspace,
+ * the same results bit for bit.  Per-tensor scaling from the amax keeps its
+ * partial maxima (at most 8192 words) in a static 32 KiB device array of the
+ * library instead of a caller workspace; every other granularity and mode
+ * needs no scratch memory at all.  The call allocates nothing.
+ *   - Each GPU holds its own copy of the array until the process ends; the
+ *     first call on a device looks up its address (do that first call
+ *     outside graph capture).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind (nothing in it needs clearing: each call writes the partials it
+ *     reads).  Per-tensor FROM_AMAX calls that may run at the same time on
+ *     one GPU (different streams without ordering) race on the array and
+ *     must be ordered by the caller; use fp8_quantize with separate
+ *     workspaces for concurrent per-tensor quantizes.
+ *   - A shape needing more partials than the array holds returns
+ *     GS_ERR_WORKSPACE (none does: the partial count is capped at 8192).
+ * Other arguments, results and errors exactly as fp8_quantize.
+ */
+gs_status fp8_quantize_no_workspace(const void *x, gs_dtype x_dtype, int64_t rows, int64_t cols,
+                                    fp8_format fmt, fp8_granularity g, fp8_scale_mode mode,
+                                    uint8_t *codes, float *scales, int32_t *nonfinite,
+                                    void *stream);
+
+/*
  * fp8_quantize_delayed -- per-tensor FP8 quantization with delayed scaling:
  * the scale applied this step comes from a history of recent amax values,
  * so the tensor is read once.  "Why FP8 training is stable", Failure 1

@@ -26,7 +26,7 @@ FP8_SCALE_FROM_AMAX, FP8_SCALE_GIVEN = 0, 1
 EXPORTS = ("gs_unscale_check", "gs_unscale_list_descriptors",
            "gs_unscale_check_sumsq_workspace_size", "gs_unscale_check_sumsq",
            "gs_update_scale", "gs_update_scale_hysteresis", "fp8_quantize_workspace_size",
-           "fp8_quantize", "fp8_quantize_delayed", "fp8_dequantize", "fp8_dequantize_bf16",
+           "fp8_quantize", "fp8_quantize_no_workspace", "fp8_quantize_delayed", "fp8_dequantize", "fp8_dequantize_bf16",
            "fp8_quantize_mx", "fp8_dequantize_mx", "gs_status_string")
 
 _lib = None
@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.fp8_quantize.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, P, P, P, P, ctypes.c_size_t, P]
         L.fp8_quantize.restype = I32
+        L.fp8_quantize_no_workspace.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, P, P, P, P]
+        L.fp8_quantize_no_workspace.restype = I32
         L.fp8_quantize_delayed.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, P, P, I32,
                                            P, P, P, P, P, ctypes.c_size_t, P]
         L.fp8_quantize_delayed.restype = I32
@@ -321,6 +324,23 @@ def fp8_quantize(x, fmt: int, gran: int, mode: int = FP8_SCALE_FROM_AMAX, codes=
     _call(dev, "fp8_quantize", lib().fp8_quantize, _ptr(x), dt, rows, cols, int(fmt), int(gran),
           int(mode), _ptr(codes), _ptr(scales), _ptr(nonfinite), _ptr(workspace),
           _bytes(workspace), _stream(stream, dev))
+    return codes, scales
+
+
+def fp8_quantize_no_workspace(x, fmt: int, gran: int, codes, scales,
+                              mode: int = FP8_SCALE_FROM_AMAX, nonfinite=None, stream=None):
+    """fp8_quantize without a workspace: the per-tensor partial maxima live
+    in the library's static device array.  codes and scales must be given
+    (nothing is allocated); same results as fp8_quantize."""
+    import torch
+    rows, cols, dev = _matrix(x, "x", (torch.bfloat16, torch.float32))
+    dt = _input_dtype(x)
+    _gpu(codes, "codes", (torch.uint8,), dev, rows * cols, exact=True)
+    _gpu(scales, "scales", (torch.float32,), dev, n_scales(rows, cols, gran))
+    _gpu(nonfinite, "nonfinite", (torch.int32,), dev, 1, optional=True)
+    _call(dev, "fp8_quantize_no_workspace", lib().fp8_quantize_no_workspace, _ptr(x), dt, rows,
+          cols, int(fmt), int(gran), int(mode), _ptr(codes), _ptr(scales), _ptr(nonfinite),
+          _stream(stream, dev))
     return codes, scales
 
 
