@@ -209,31 +209,26 @@ CEIL_POLICY = ("plain", "nt", "sc1nt")
 
 
 def measure_ceilings(dev, specs, tev, reps=5):
-    """Best rate of each access pattern over a sweep of launch shapes, from
-    the streaming kernels of libgsceil.so on flat buffers of the given
-    sizes.  specs: (name, pattern, n) with n elements (read / write: bytes).
-    Each variant is launched once untimed, then `reps` times, each launch
-    between two HIP events on the current stream (the events of the
-    unscale's own timing); the median is the variant's time, the fastest
-    variant the ceiling.  Working sets below 512 MB would otherwise be
-    served partly by the 256 MB infinity cache on a repeat, so each of
-    their launches follows a 1 GiB write and a 1 GiB read (stream-ordered,
-    untimed): their inputs come from HBM, like those of the benchmark
-    step's kernels, which follow the 48 GB unscale."""
+    """Best sustained rate of each access pattern over a sweep of launch
+    shapes, from the streaming kernels of libgsceil.so on flat buffers of
+    the given sizes.  specs: (name, pattern, n) with n elements (read /
+    write: bytes).  Launches run back to back, each between two HIP events
+    on the current stream (the events of the unscale's own timing), so each
+    pays for the previous launch's write drain, as the step's kernels do.  A
+    working set below 4 GiB would partly stay in the 256 MB infinity cache
+    and its writes drain after its end event, so such a pattern cycles
+    through k buffer sets (k x working set >= 4 GiB): every launch reads
+    from HBM.  Each variant: one untimed round over the sets, then
+    max(reps, k) timed launches; the median is its time, the fastest
+    variant the ceiling."""
     import ctypes
 
     import numpy as np
     import torch
     L = ctypes.CDLL(CEIL_LIB)
     L.gsc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                              ctypes.c_void_p]
-    junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    junk_rd = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-
-    def flush():
-        junk.fill_(1.0)
-        junk_rd.sum()
     L.gsc_stream.restype = ctypes.c_int
     stream = torch.cuda.current_stream().cuda_stream
     out = {}
@@ -241,12 +236,14 @@ def measure_ceilings(dev, specs, tev, reps=5):
         p = CEIL_PATTERNS[pattern]
         src_bytes = {0: n, 1: 0, 2: 2 * n, 3: 2 * n, 4: n}[p]
         dst_bytes = {0: 1024, 1: n, 2: 4 * n, 3: n, 4: 4 * n}[p]
-        src = torch.empty(max(src_bytes, 16), dtype=torch.uint8, device=dev)
-        dst = torch.empty(dst_bytes, dtype=torch.uint8, device=dev)
+        work = src_bytes + dst_bytes
+        k = max(1, min(16, -(-(4 << 30) // work)))
+        sets = [(torch.empty(max(src_bytes, 16), dtype=torch.uint8, device=dev),
+                 torch.empty(dst_bytes, dtype=torch.uint8, device=dev)) for _ in range(k)]
         moved = src_bytes + (0 if p == 0 else dst_bytes)
-        cold = src_bytes + dst_bytes < (512 << 20)
         best = None
-        for unroll in (1, 2, 4, 8):
+        shapes = [(1, 0)] + [(u, lay) for u in (2, 4, 8) for lay in (0, 1)]
+        for unroll, layout in shapes:
             for ntl in (0, 1):
                 if p == 1 and ntl:
                     continue                       # no loads to vary
@@ -254,34 +251,31 @@ def measure_ceilings(dev, specs, tev, reps=5):
                     if p == 0 and policy:
                         continue                   # no stores to vary
                     for occ in (0, 7, 5):
-                        args = (p, src.data_ptr(), dst.data_ptr(), n, unroll, ntl, policy, occ,
-                                stream)
-                        rc = L.gsc_stream(*args)
-                        if rc != 0:
-                            raise RuntimeError("gsc_stream%r returned %d" % (args[:1] + args[3:8], rc))
-                        evs = [(tev.new(), tev.new()) for _ in range(reps)]
-                        for a, b in evs:
-                            if cold:
-                                flush()
+                        args = [(p, s.data_ptr(), d.data_ptr(), n, unroll, layout, ntl, policy,
+                                 occ, stream) for s, d in sets]
+                        for a in args:
+                            rc = L.gsc_stream(*a)
+                            if rc != 0:
+                                raise RuntimeError("gsc_stream%r returned %d" % (a[:1] + a[3:9], rc))
+                        evs = [(tev.new(), tev.new()) for _ in range(max(reps, k))]
+                        for j, (a, b) in enumerate(evs):
                             tev.record(a, stream)
-                            L.gsc_stream(*args)
+                            L.gsc_stream(*args[j % k])
                             tev.record(b, stream)
                         torch.cuda.synchronize()
                         ms = float(np.median([tev.elapsed_ms(a, b) for a, b in evs]))
                         if best is None or ms < best[0]:
-                            best = (ms, unroll, ntl, policy, occ)
-        ms, unroll, ntl, policy, occ = best
+                            best = (ms, unroll, layout, ntl, policy, occ)
+        ms, unroll, layout, ntl, policy, occ = best
         out[name] = {"GBps": round(moved / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4),
-                     "bytes": moved, "elements": n, "pattern": pattern,
-                     "inputs": "from HBM (flushed before each launch)" if cold else
-                               "from HBM (working set far above the caches)",
-                     "variant": "unroll %d, %s loads, %s stores, %s" % (
-                         unroll, "non-temporal" if ntl else "plain", CEIL_POLICY[policy],
+                     "bytes": moved, "elements": n, "pattern": pattern, "buffer_sets": k,
+                     "variant": "unroll %d (%s), %s loads, %s stores, %s" % (
+                         unroll, "lane-contiguous units" if layout else "wave-contiguous units",
+                         "non-temporal" if ntl else "plain", CEIL_POLICY[policy],
                          "no occupancy cap" if occ == 0 else "%d workgroups per CU" % occ)}
         log("ceiling %s: %.0f GB/s (%s)" % (name, out[name]["GBps"], out[name]["variant"]))
-        del src, dst
+        del sets
         torch.cuda.empty_cache()
-    del junk, junk_rd
     return out
 
 
@@ -393,13 +387,15 @@ def measure_configs(dev):
         del x, codes, scales, out
     res["per_tensor_8192"] = pt
     # 4 GiB special values, scales from the block amax
+    tev = TimingEvents()
     sv = measure_special_values(dev, [sp.name for sp in synth.special_values_4gib()],
-                                ("e4m3", "e5m2"), ("cold", "b2b"), 20)
+                                ("e4m3", "e5m2"), ("cold", "b2b"), 20, tev)
+    tev.destroy()
     res["special_4gib"] = sv
     return res
 
 
-def measure_special_values(dev, tensors, fmts, phases, reps):
+def measure_special_values(dev, tensors, fmts, phases, reps, tev=None):
     """The four 16384x32768 BF16 special-value tensors: quantize with scales
     from the amax (per-tensor, 1x128, 128x128) and the FP32 dequantize, per
     tensor x format x granularity, `reps` launches each.  Phase "cold": a
@@ -407,7 +403,10 @@ def measure_special_values(dev, tensors, fmts, phases, reps):
     launch, so that the previous launch's writes have drained and the cache
     holds clean lines of other data; phase "b2b": the launches back to back,
     each paying for the previous one's write drain.  Medians of HIP-event
-    times; GB/s from the algorithmic bytes."""
+    times; GB/s from the algorithmic bytes.  With `tev` (TimingEvents), the
+    sustained ceilings of the 2 B -> 1 B and 1 B -> 4 B patterns at this
+    size are measured too, and each block-granularity entry gets its
+    fraction of them."""
     import torch
 
     import loss_scaling_fp8_amd as gs
@@ -460,6 +459,15 @@ def measure_special_values(dev, tensors, fmts, phases, reps):
         torch.cuda.empty_cache()
     sv["note"] = ("per-tensor runs two passes over the input (amax, then cast): its GB/s "
                   "counts the algorithmic 3 B/element, the traffic is 5 B/element")
+    if tev is not None:
+        n = synth.special_values_4gib()[0].rows * synth.special_values_4gib()[0].cols
+        ceil = measure_ceilings(dev, [("narrow_2to1", "narrow_2to1", n),
+                                      ("expand_1to4", "expand_1to4", n)], tev)
+        for key, e in sv.items():
+            if key != "note" and "/tensor/" not in key:
+                e["quant_frac_of_ceiling"] = round(e["quant_GBps"] / ceil["narrow_2to1"]["GBps"], 4)
+                e["dequant_frac_of_ceiling"] = round(e["dequant_GBps"] / ceil["expand_1to4"]["GBps"], 4)
+        sv["ceilings"] = ceil
     return sv
 
 
@@ -476,8 +484,8 @@ def main():
                          "configurations (reported under \"configs\")")
     ap.add_argument("--special-values", nargs=3, metavar=("TENSOR", "FMT", "PHASE"),
                     help="only time the 4 GiB special-value quantize/dequantize for one "
-                         "tensor (mix, anchored, saturation, random), format (e4m3, e5m2) "
-                         "and phase (cold, b2b), 20 launches each (for per-configuration "
+                         "tensor (mix, anchored, saturation, random), format (e4m3, e5m2, "
+                         "both) and phase (cold, b2b), 20 launches each (for per-configuration "
                          "kernel-trace profiles); prints one JSON object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 6 plain copy kernels of 1 GiB (for HBM counter calibration)")
@@ -505,11 +513,16 @@ def main():
     torch.cuda.set_device(dev)
     if args.special_values:
         t, f, ph = args.special_values
-        if t not in ("mix", "anchored", "saturation", "random") or f not in ("e4m3", "e5m2") \
-                or ph not in ("cold", "b2b"):
+        if t not in ("mix", "anchored", "saturation", "random") or \
+                f not in ("e4m3", "e5m2", "both") or ph not in ("cold", "b2b"):
             ap.error("--special-values TENSOR FMT PHASE: see --help")
         gs.lib()
-        print(json.dumps({"special_4gib": measure_special_values(dev, (t,), (f,), (ph,), 20)}))
+        fmts = ("e4m3", "e5m2") if f == "both" else (f,)
+        tev = None if args.no_ceilings else TimingEvents()
+        sv = measure_special_values(dev, (t,), fmts, (ph,), 20, tev)
+        if tev is not None:
+            tev.destroy()
+        print(json.dumps({"special_4gib": sv}))
         return
     if args.copy_calibration:
         # int32 -> float32 converting copy: an elementwise kernel reading and

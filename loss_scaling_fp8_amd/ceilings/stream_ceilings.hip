@@ -4,9 +4,10 @@
 // for measurement: the benchmark times every variant below and reports each
 // library kernel's rate as a fraction of the best rate of its pattern.
 //
-// Patterns (n = elements; a lane handles U units per chunk, unit index
-// u * 256 + lane within a chunk of 256 * U units, so every wave-wide access
-// is contiguous):
+// Patterns (n = elements; a lane handles U units per chunk of 256 * U
+// units: unit u * 256 + lane (layout 0: every wave-wide access is
+// contiguous) or lane * U + u (layout 1: each lane's U units are
+// contiguous, the layout of the quantizers' lanes)):
 //   0 read only        16-byte loads, XOR-folded (n = bytes / 16 units)
 //   1 write only       16-byte stores             (n = bytes / 16 units)
 //   2 2 B -> 4 B       4 FP16 -> 4 FP32 per unit (8-byte load, 16-byte store):
@@ -16,7 +17,7 @@
 //                      quantizers' pattern
 //   4 1 B -> 4 B       4 bytes -> 4 FP32 per unit (4-byte load, 16-byte
 //                      store): the FP32 dequantizers' pattern
-// Variants: U in {1, 2, 4, 8}; plain or non-temporal loads; store policy 0
+// Variants: U in {1, 2, 4, 8}; layout 0 or 1; plain or non-temporal loads; store policy 0
 // plain, 1 non-temporal, 2 a buffer store with the device-scope
 // non-temporal policy (sc1 nt); and an occupancy cap of k workgroups per CU
 // (0 = none), made by reserving LDS the kernel does not use.
@@ -63,7 +64,7 @@ __device__ __forceinline__ uint32_t hi_bytes(uint32_t a, uint32_t b) {
     return ((a >> 8) & 0xFFu) | ((a >> 16) & 0xFF00u) | ((b << 8) & 0xFF0000u) | (b & 0xFF000000u);
 }
 
-template <int PATTERN, int U, int POLICY, bool NTL>
+template <int PATTERN, int U, int POLICY, bool NTL, int LAYOUT>
 __global__ __launch_bounds__(kThreads)
 void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t nunits,
                    uint32_t *__restrict__ sink) {
@@ -78,7 +79,7 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
             u32x4 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 v[u] = base + i < nunits ? get<NTL>(s + i) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
@@ -88,7 +89,7 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
             const u32x4 v = {uint32_t(c), 1u, 2u, 3u};
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 if (base + i < nunits) put16<POLICY>(d, uint32_t(i) * 16u, v);
             }
         } else if constexpr (PATTERN == 2) {
@@ -97,12 +98,12 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
             u32x2 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 v[u] = base + i < nunits ? get<NTL>(s + i) : u32x2{0, 0};
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 const f32x4 y = {h2f(v[u].x & 0xFFFFu), h2f(v[u].x >> 16), h2f(v[u].y & 0xFFFFu),
                                  h2f(v[u].y >> 16)};
                 if (base + i < nunits) put16<POLICY>(d, uint32_t(i) * 16u, __builtin_bit_cast(u32x4, y));
@@ -113,13 +114,13 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
             u32x4 a[U], b[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 a[u] = base + i < nunits ? get<NTL>(s + 2 * i) : u32x4{0, 0, 0, 0};
                 b[u] = base + i < nunits ? get<NTL>(s + 2 * i + 1) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 const u32x4 o = {hi_bytes(a[u].x, a[u].y), hi_bytes(a[u].z, a[u].w),
                                  hi_bytes(b[u].x, b[u].y), hi_bytes(b[u].z, b[u].w)};
                 if (base + i < nunits) put16<POLICY>(d, uint32_t(i) * 16u, o);
@@ -130,12 +131,12 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
             uint32_t v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 v[u] = base + i < nunits ? get<NTL>(s + i) : 0u;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = u * kThreads + threadIdx.x;
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
                 const f32x4 y = {float(v[u] & 0xFFu), float((v[u] >> 8) & 0xFFu),
                                  float((v[u] >> 16) & 0xFFu), float(v[u] >> 24)};
                 if (base + i < nunits) put16<POLICY>(d, uint32_t(i) * 16u, __builtin_bit_cast(u32x4, y));
@@ -148,51 +149,55 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
 // elements per unit of each pattern (read/write: bytes per unit)
 constexpr int64_t kElemsPerUnit[5] = {16, 16, 4, 16, 4};
 
-template <int PATTERN, int U, bool NTL>
+template <int PATTERN, int U, bool NTL, int LAYOUT>
 hipError_t launch_u(int policy, const void *src, void *dst, int64_t nunits, uint32_t *sink,
                     dim3 grid, unsigned lds, hipStream_t s) {
     if (policy == 0)
-        hipLaunchKernelGGL((stream_kernel<PATTERN, U, 0, NTL>), grid, dim3(kThreads), lds, s, src, dst, nunits, sink);
+        hipLaunchKernelGGL((stream_kernel<PATTERN, U, 0, NTL, LAYOUT>), grid, dim3(kThreads), lds, s, src, dst, nunits, sink);
     else if (policy == 1)
-        hipLaunchKernelGGL((stream_kernel<PATTERN, U, 1, NTL>), grid, dim3(kThreads), lds, s, src, dst, nunits, sink);
+        hipLaunchKernelGGL((stream_kernel<PATTERN, U, 1, NTL, LAYOUT>), grid, dim3(kThreads), lds, s, src, dst, nunits, sink);
     else
-        hipLaunchKernelGGL((stream_kernel<PATTERN, U, 2, NTL>), grid, dim3(kThreads), lds, s, src, dst, nunits, sink);
+        hipLaunchKernelGGL((stream_kernel<PATTERN, U, 2, NTL, LAYOUT>), grid, dim3(kThreads), lds, s, src, dst, nunits, sink);
     return hipGetLastError();
 }
 
 template <int PATTERN, int U>
-hipError_t launch_l(bool ntl, int policy, const void *src, void *dst, int64_t nunits,
+hipError_t launch_l(bool ntl, int layout, int policy, const void *src, void *dst, int64_t nunits,
                     uint32_t *sink, dim3 grid, unsigned lds, hipStream_t s) {
-    return ntl ? launch_u<PATTERN, U, true>(policy, src, dst, nunits, sink, grid, lds, s)
-               : launch_u<PATTERN, U, false>(policy, src, dst, nunits, sink, grid, lds, s);
+    if (layout == 0)
+        return ntl ? launch_u<PATTERN, U, true, 0>(policy, src, dst, nunits, sink, grid, lds, s)
+                   : launch_u<PATTERN, U, false, 0>(policy, src, dst, nunits, sink, grid, lds, s);
+    return ntl ? launch_u<PATTERN, U, true, 1>(policy, src, dst, nunits, sink, grid, lds, s)
+               : launch_u<PATTERN, U, false, 1>(policy, src, dst, nunits, sink, grid, lds, s);
 }
 
 template <int PATTERN>
-hipError_t launch_p(int unroll, bool ntl, int policy, const void *src, void *dst, int64_t nunits,
-                    uint32_t *sink, unsigned lds, hipStream_t s) {
+hipError_t launch_p(int unroll, bool ntl, int layout, int policy, const void *src, void *dst,
+                    int64_t nunits, uint32_t *sink, unsigned lds, hipStream_t s) {
     int64_t g = (nunits + int64_t(kThreads) * unroll - 1) / (int64_t(kThreads) * unroll);
     if (g < 1) g = 1;
     if (g > kMaxGrid) g = kMaxGrid;
     const dim3 grid((uint32_t)g);
     switch (unroll) {
-        case 1: return launch_l<PATTERN, 1>(ntl, policy, src, dst, nunits, sink, grid, lds, s);
-        case 2: return launch_l<PATTERN, 2>(ntl, policy, src, dst, nunits, sink, grid, lds, s);
-        case 4: return launch_l<PATTERN, 4>(ntl, policy, src, dst, nunits, sink, grid, lds, s);
-        default: return launch_l<PATTERN, 8>(ntl, policy, src, dst, nunits, sink, grid, lds, s);
+        case 1: return launch_l<PATTERN, 1>(ntl, layout, policy, src, dst, nunits, sink, grid, lds, s);
+        case 2: return launch_l<PATTERN, 2>(ntl, layout, policy, src, dst, nunits, sink, grid, lds, s);
+        case 4: return launch_l<PATTERN, 4>(ntl, layout, policy, src, dst, nunits, sink, grid, lds, s);
+        default: return launch_l<PATTERN, 8>(ntl, layout, policy, src, dst, nunits, sink, grid, lds, s);
     }
 }
 
 }  // namespace
 
 // One launch of pattern `pattern` over n elements (read / write: n bytes)
-// on `stream`, with non-temporal loads when nt_loads is 1.  src / dst are device buffers of the pattern's sizes (16-byte
+// on `stream`, in unit layout `layout`, with non-temporal loads when
+// nt_loads is 1.  src / dst are device buffers of the pattern's sizes (16-byte
 // aligned; dst of pattern 0 is a 1 KiB sink).  n must be a whole number of
 // units and below 2^31 units per 16-byte store offset within a chunk (always
 // true here).  Returns 0, -1 for bad arguments, or the HIP error code.
 extern "C" int gsc_stream(int pattern, const void *src, void *dst, int64_t n, int unroll,
-                          int nt_loads, int policy, int wgs_per_cu, void *stream) {
+                          int layout, int nt_loads, int policy, int wgs_per_cu, void *stream) {
     if (pattern < 0 || pattern > 4 || n < 0 || policy < 0 || policy > 2 || wgs_per_cu < 0 ||
-        (nt_loads != 0 && nt_loads != 1))
+        (nt_loads != 0 && nt_loads != 1) || (layout != 0 && layout != 1))
         return -1;
     if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return -1;
     if (n % kElemsPerUnit[pattern] != 0) return -1;
@@ -213,11 +218,11 @@ extern "C" int gsc_stream(int pattern, const void *src, void *dst, int64_t n, in
     uint32_t *sink = static_cast<uint32_t *>(dst);
     hipError_t e;
     switch (pattern) {
-        case 0: e = launch_p<0>(unroll, nt_loads == 1, policy, src, dst, nunits, sink, lds, s); break;
-        case 1: e = launch_p<1>(unroll, nt_loads == 1, policy, src, dst, nunits, sink, lds, s); break;
-        case 2: e = launch_p<2>(unroll, nt_loads == 1, policy, src, dst, nunits, sink, lds, s); break;
-        case 3: e = launch_p<3>(unroll, nt_loads == 1, policy, src, dst, nunits, sink, lds, s); break;
-        default: e = launch_p<4>(unroll, nt_loads == 1, policy, src, dst, nunits, sink, lds, s); break;
+        case 0: e = launch_p<0>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
+        case 1: e = launch_p<1>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
+        case 2: e = launch_p<2>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
+        case 3: e = launch_p<3>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
+        default: e = launch_p<4>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
     }
     return e == hipSuccess ? 0 : int(e);
 }

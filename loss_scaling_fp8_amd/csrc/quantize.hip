@@ -45,6 +45,7 @@
 //  * The max-abs is taken on bit patterns: for non-negative floats unsigned
 //    integer order is numeric order, and BF16 halves are maxed pairwise.
 #include "device_fp8.hpp"
+#include <atomic>
 #include <type_traits>
 #include "gs_internal.hpp"
 
@@ -69,6 +70,30 @@
 #endif
 #ifndef Q128_THREADS
 #define Q128_THREADS 256
+#endif
+// per-tensor scaling of a cache-resident tensor: partial maxima of the amax
+// pass, pieces in flight per lane there and its load policy, and pieces
+// per lane of the cast (which reduces the partials once per workgroup)
+#ifndef GS_PT_FOLD_PARTS
+#define GS_PT_FOLD_PARTS 1024
+#endif
+#ifndef GS_PT_AMAX_U
+#define GS_PT_AMAX_U 2
+#endif
+#ifndef GS_PT_AMAX_NT
+#define GS_PT_AMAX_NT 0
+#endif
+#ifndef GS_PT_CAST_PIECES
+#define GS_PT_CAST_PIECES 2
+#endif
+// block quantizers: workgroups per CU (0 = as many as registers allow),
+// capped by reserving LDS the kernels do not use; measured best: 6 for the
+// row-block kernel (1x128, 1x32, MX), 5 for 128x128
+#ifndef GS_Q1_WGS_PER_CU
+#define GS_Q1_WGS_PER_CU 6
+#endif
+#ifndef GS_Q128_WGS_PER_CU
+#define GS_Q128_WGS_PER_CU 5
 #endif
 
 namespace gsk {
@@ -403,13 +428,20 @@ void amax_partials_kernel(const IN *__restrict__ x, int64_t n, uint32_t *__restr
         }
     } else {
         constexpr int NV = kStep * int(sizeof(IN)) / 16;
-        for (int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x; b < nunits;
-             b += int64_t(gridDim.x) * 256) {
-            LaneData<IN, NV> L;
-            L.template load<false>(x + b * kStep);
-            uint32_t a;
-            nf |= L.absmax(a);
-            m = max(m, a);
+        constexpr int U = GS_PT_AMAX_U;
+        for (int64_t b0 = int64_t(blockIdx.x) * 256 * U + threadIdx.x; b0 < nunits;
+             b0 += int64_t(gridDim.x) * 256 * U) {
+            LaneData<IN, NV> L[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (b0 + u * 256 < nunits) L[u].template load<GS_PT_AMAX_NT>(x + (b0 + u * 256) * kStep);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (b0 + u * 256 < nunits) {
+                    uint32_t a;
+                    nf |= L[u].absmax(a);
+                    m = max(m, a);
+                }
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nunits * kStep) {     // ragged tail
@@ -473,7 +505,7 @@ void amax_finalize_kernel(const uint32_t *__restrict__ partials, int nparts,
 // Streamed tensors keep pass 2: capping their amax pass at kFoldParts
 // workgroups cost them 5%.  (Loading the first piece before the fold, to
 // overlap the two, gained nothing; 2048 partials cost 6%.)
-constexpr int kFoldParts = 1024;
+constexpr int kFoldParts = GS_PT_FOLD_PARTS;
 static_assert(kFoldParts % 256 == 0 && kFoldParts <= kPartialSlots, "fold partials");
 
 template <int FMT, bool GIVEN, typename IN, bool EMIT = false, bool FOLD = false>
@@ -744,6 +776,23 @@ void dequant_tiles_kernel(const uint8_t *__restrict__ codes, int64_t n, int64_t 
 
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
+// Dynamic LDS that caps a block quantizer at `wgs` workgroups per CU (0: no
+// cap), from the device's LDS per CU (queried once per device).
+inline unsigned quant_lds_reserve(int wgs) {
+    if (wgs <= 0) return 0;
+    static std::atomic<int> lds_per_cu[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int lds = lds_per_cu[dev].load(std::memory_order_relaxed);
+    if (lds <= 0) {
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess || lds <= 0)
+            return 0;
+        lds_per_cu[dev].store(lds, std::memory_order_relaxed);
+    }
+    return unsigned(lds) / unsigned(wgs + 1) + 1024u;
+}
+
 inline uint32_t grid_for(int64_t work_items, int64_t per_wg) {
     int64_t g = (work_items + per_wg - 1) / per_wg;
     if (g < 1) g = 1;
@@ -757,8 +806,9 @@ hipError_t quantize_rows(const IN *x, int64_t n, uint8_t *codes, void *scales,
     const int64_t nblocks = n / BLOCK;
     if (nblocks == 0) return hipSuccess;
     hipLaunchKernelGGL((quant_row_blocks_kernel<FMT, MODE, IN, BLOCK>),
-                       dim3(grid_for(nblocks, 256 / (BLOCK / 32))), dim3(256), 0, stream, x,
-                       nblocks, codes, scales, nonfinite);
+                       dim3(grid_for(nblocks, 256 / (BLOCK / 32))), dim3(256),
+                       quant_lds_reserve(GS_Q1_WGS_PER_CU), stream, x, nblocks, codes, scales,
+                       nonfinite);
     return hipGetLastError();
 }
 
@@ -775,8 +825,8 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
         const int64_t tpr = cols / 128, ntiles = (rows / 128) * tpr;
         if (ntiles == 0) return hipSuccess;
         hipLaunchKernelGGL((quant_128x128_kernel<FMT, MODE, IN>), dim3(grid_for(ntiles, 1)),
-                           dim3(Q128_THREADS), 0, stream, x, cols, tpr, ntiles, codes, scales,
-                           nonfinite);
+                           dim3(Q128_THREADS), quant_lds_reserve(GS_Q128_WGS_PER_CU), stream, x,
+                           cols, tpr, ntiles, codes, scales, nonfinite);
         return hipGetLastError();
     }
     // per-tensor: partial maxima, the scale, the cast (given mode: the cast);
@@ -797,8 +847,8 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
         if (e != hipSuccess) return e;
         if (!stream_big) {
             hipLaunchKernelGGL((quant_tensor_kernel<FMT, false, IN, false, true>),
-                               dim3(grid_for(n / 32, 256)), dim3(256), 0, stream, x, n, codes,
-                               scales, nonfinite, partials, (int)p);
+                               dim3(grid_for(n / 32, 256 * GS_PT_CAST_PIECES)), dim3(256), 0,
+                               stream, x, n, codes, scales, nonfinite, partials, (int)p);
             return hipGetLastError();
         }
         hipLaunchKernelGGL((amax_finalize_kernel<FMT>), dim3(1), dim3(1024), 0, stream, partials,
