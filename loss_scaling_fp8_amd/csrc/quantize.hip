@@ -89,6 +89,17 @@
 // block quantizers: workgroups per CU (0 = as many as registers allow),
 // capped by reserving LDS the kernels do not use; measured best: 6 for the
 // row-block kernel (1x128, 1x32, MX), 5 for 128x128
+// FP32-output dequantizers: groups of 4 codes per lane per work item (the
+// linear walk; the 128x128 walk), and workgroups per CU (0 = no cap)
+#ifndef GS_DQ_UNROLL_F32
+#define GS_DQ_UNROLL_F32 2
+#endif
+#ifndef GS_DQT_UNROLL_F32
+#define GS_DQT_UNROLL_F32 4
+#endif
+#ifndef GS_DQ_WGS_PER_CU
+#define GS_DQ_WGS_PER_CU 0
+#endif
 #ifndef GS_Q1_WGS_PER_CU
 #define GS_Q1_WGS_PER_CU 6
 #endif
@@ -628,9 +639,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <typename OUT>
 struct DqGroup {
     static constexpr int kCodes = sizeof(OUT) == 4 ? 4 : 8;    // codes per lane per group
-    // groups per lane per work item of the flat walk (BF16: 2, measured
-    // back to back 1.3% ahead of 4 on 16384x7168 codes)
-    static constexpr int kUnroll = sizeof(OUT) == 4 ? 4 : 2;
+    // groups per lane per work item of the flat walk.  BF16: 2, measured
+    // back to back 1.3% ahead of 4 on 16384x7168 codes.  FP32, linear walk:
+    // 2, ahead of 4 by 7% cold and 10% on 16384x32768 codes (8 lost 6%);
+    // FP32, 128x128 walk: 4 (2 was within +-2%).
+    static constexpr int kUnroll = sizeof(OUT) == 4 ? GS_DQ_UNROLL_F32 : 2;
+    static constexpr int kUnrollTiles = sizeof(OUT) == 4 ? GS_DQT_UNROLL_F32 : 2;
     typedef typename std::conditional<kCodes == 4, uint32_t, u32x2>::type Word;
 };
 
@@ -737,7 +751,7 @@ __global__ __launch_bounds__(256)
 void dequant_tiles_kernel(const uint8_t *__restrict__ codes, int64_t n, int64_t cols,
                           uint32_t nb, float inv_nb, const float *__restrict__ scales,
                           OUT *__restrict__ out) {
-    constexpr int U = DqGroup<OUT>::kUnroll;
+    constexpr int U = DqGroup<OUT>::kUnrollTiles;
     constexpr int kCodes = DqGroup<OUT>::kCodes;
     typedef typename DqGroup<OUT>::Word Word;
     const int64_t ngroups = n / kCodes;
@@ -886,20 +900,22 @@ hipError_t dequantize_fmt(const uint8_t *codes, int64_t rows, int64_t cols, int 
     const int64_t n = rows * cols;
     if (n == 0) return hipSuccess;
     const dim3 grid(grid_for(n / DqGroup<OUT>::kCodes, 256 * DqGroup<OUT>::kUnroll));
+    const unsigned dq_lds = sizeof(OUT) == 4 ? quant_lds_reserve(GS_DQ_WGS_PER_CU) : 0u;
     if (gran == FP8_BLOCK_128x128) {
+        const dim3 tgrid(grid_for(n / DqGroup<OUT>::kCodes, 256 * DqGroup<OUT>::kUnrollTiles));
         const uint32_t nb = uint32_t(cols / 128);              // <= 2^24
-        hipLaunchKernelGGL((dequant_tiles_kernel<FMT, OUT>), grid, dim3(256), 0, stream, codes, n,
+        hipLaunchKernelGGL((dequant_tiles_kernel<FMT, OUT>), tgrid, dim3(256), dq_lds, stream, codes, n,
                            cols, nb, 1.0f / float(nb), scales, out);
         return hipGetLastError();
     }
     if (gran == FP8_BLOCK_1x128)
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 1, OUT>), grid, dim3(256), 0, stream, codes,
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 1, OUT>), grid, dim3(256), dq_lds, stream, codes,
                            n, scales, out);
     else if (gran == FP8_BLOCK_1x32)
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 2, OUT>), grid, dim3(256), 0, stream, codes,
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 2, OUT>), grid, dim3(256), dq_lds, stream, codes,
                            n, scales, out);
     else
-        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 0, OUT>), grid, dim3(256), 0, stream, codes,
+        hipLaunchKernelGGL((dequant_linear_kernel<FMT, 0, OUT>), grid, dim3(256), dq_lds, stream, codes,
                            n, scales, out);
     return hipGetLastError();
 }
@@ -908,8 +924,10 @@ template <int FMT>
 hipError_t dequantize_mx_fmt(const uint8_t *codes, int64_t n, const uint8_t *scales, float *out,
                              hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL((dequant_linear_kernel<FMT, 3, float>), dim3(grid_for(n / 4, 256 * 4)),
-                       dim3(256), 0, stream, codes, n, scales, out);
+    hipLaunchKernelGGL((dequant_linear_kernel<FMT, 3, float>),
+                       dim3(grid_for(n / 4, 256 * DqGroup<float>::kUnroll)),
+                       dim3(256), quant_lds_reserve(GS_DQ_WGS_PER_CU), stream, codes, n, scales,
+                       out);
     return hipGetLastError();
 }
 
