@@ -23,6 +23,8 @@ def _host_calls():
         "gs_update_scale": lambda: gs.gs_update_scale(S, i32, i32),
         "gs_update_scale_hysteresis": lambda: gs.gs_update_scale_hysteresis(S, i32, i32, i32),
         "fp8_quantize": lambda: gs.fp8_quantize(x, gs.FP8_E4M3, gs.FP8_BLOCK_1x128),
+        "fp8_quantize_no_workspace": lambda: gs.fp8_quantize_no_workspace(
+            x, gs.FP8_E4M3, gs.FP8_PER_TENSOR, codes, S),
         "fp8_quantize_delayed": lambda: gs.fp8_quantize_delayed(
             x, gs.FP8_E4M3, S, torch.zeros(4, dtype=F32), i32),
         "fp8_dequantize": lambda: gs.fp8_dequantize(codes, gs.FP8_E4M3, gs.FP8_BLOCK_1x128, sc),
