@@ -287,6 +287,25 @@ static void test_quantize(hipStream_t st) {
                       memcmp(out16, rout16, (size_t)n * 2) == 0,
                   what);
         }
+        /* per-tensor scaling without a workspace (the library's static scratch) */
+        {
+            int32_t nf = 0, rnf = 0;
+            HIPCHECK(hipMemset(dnf, 0, 4));
+            const gs_status s = fp8_quantize_no_workspace(dx, GS_BF16, R, C, (fp8_format)fmt,
+                                                          FP8_PER_TENSOR, FP8_SCALE_FROM_AMAX,
+                                                          dcodes, dsc, dnf, st);
+            orc_quantize(hx, GS_BF16, R, C, fmt, FP8_PER_TENSOR, FP8_SCALE_FROM_AMAX, rcodes, rsc,
+                         &rnf);
+            HIPCHECK(hipStreamSynchronize(st));
+            from_dev(codes, dcodes, (size_t)n);
+            from_dev(sc, dsc, 4);
+            from_dev(&nf, dnf, 4);
+            snprintf(what, sizeof what, "fmt %d per-tensor without a workspace: codes, scale, flag",
+                     fmt);
+            check(s == GS_OK && memcmp(codes, rcodes, (size_t)n) == 0 && memcmp(sc, rsc, 4) == 0 &&
+                      nf == rnf && nf == 1,
+                  what);
+        }
         /* MX blocks with E8M0 scale bytes */
         {
             uint8_t *dmx = (uint8_t *)dsc;         /* n / 32 bytes fit */

@@ -4,7 +4,8 @@ calls every compute entry point of include/gs.h on a stream of its own, and
 compares each result bit for bit with the C oracle linked beside it: the
 unscale and the update over three steps (an Inf on the second), the exact
 sum of squares, the hysteresis policy, quantize and FP32 / BF16 dequantize
-at every granularity in both formats, MX blocks and three delayed-scaling
+at every granularity in both formats, the per-tensor quantize without a
+workspace, MX blocks and three delayed-scaling
 steps.  No Python, torch or ctypes between the caller and the library."""
 import os
 import subprocess

@@ -15,7 +15,10 @@ Workloads (seeded, synthetic; see synth/):
   * 8192x8192 per-tensor E4M3 (0.1% x1000 outliers) and E5M2 (Laplace);
   * four 16384x32768 special-value tensors: every granularity, both
     formats, scales from the amax and given scales of 1, with dequantize;
-  * 1x32 / MX blocks and matrices past 2^32 elements: sampled blocks.
+  * 1x32 and MX 1x32 blocks on the activation shape and the special-value
+    tensors;
+  * one FP16 gradient tensor past 2^32 elements (unscale and the exact sum of
+    squares) and one 32896x131072 BF16 matrix (1x128, 128x128, MX).
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -30,7 +33,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-PT, B1, B128 = gs.FP8_PER_TENSOR, gs.FP8_BLOCK_1x128, gs.FP8_BLOCK_128x128
+PT, B1, B128, B32 = gs.FP8_PER_TENSOR, gs.FP8_BLOCK_1x128, gs.FP8_BLOCK_128x128, gs.FP8_BLOCK_1x32
 
 # host threads for the oracle (its C calls release the GIL): the job's share
 _THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -67,45 +70,6 @@ def test_generators_identical_on_cpu_and_gpu(dev):
         assert torch.equal(g.gen(t, idx), g.gen(t, idx.to(dev)).cpu())
 
 
-def _check_blocks(x_spec, codes, scales, deq, gran, fmt, rng, nsample):
-    """Sampled blocks of device tensors codes/scales/deq against the oracle
-    run on the same block regenerated on the host; returns the number of
-    blocks checked."""
-    rows, cols = x_spec.rows, x_spec.cols
-    checked = 0
-    if gran == B1:
-        nb = rows * (cols // 128)
-        blocks = np.unique(np.concatenate([rng.integers(0, nb, nsample), [0, nb - 1]]))
-        for b in blocks:
-            r, j = divmod(int(b), cols // 128)
-            idx = torch.arange(r * cols + j * 128, r * cols + j * 128 + 128)
-            xb = x_spec.gen(idx).numpy().astype(np.uint16).reshape(1, 128)
-            rc, rs, _ = oracle.quantize(xb, fmt, PT)
-            sl = (slice(r, r + 1), slice(j * 128, (j + 1) * 128))
-            assert np.array_equal(codes[sl].cpu().numpy(), rc), b
-            assert _u32(scales[r, j:j + 1])[0] == rs.view(np.uint32)[0], b
-            rd = oracle.dequantize(rc, fmt, PT, rs)
-            assert np.array_equal(_u32(deq[sl]).reshape(-1), rd.reshape(-1).view(np.uint32)), b
-            checked += 1
-    else:
-        tpr = cols // 128
-        nt = (rows // 128) * tpr
-        tiles = np.unique(np.concatenate([rng.integers(0, nt, nsample), [0, nt - 1]]))
-        for t in tiles:
-            ti, tj = divmod(int(t), tpr)
-            r = torch.arange(ti * 128, ti * 128 + 128)[:, None]
-            c = torch.arange(tj * 128, tj * 128 + 128)[None, :]
-            xb = x_spec.gen((r * cols + c).reshape(-1)).numpy().astype(np.uint16).reshape(128, 128)
-            rc, rs, _ = oracle.quantize(xb, fmt, PT)
-            sl = (slice(ti * 128, ti * 128 + 128), slice(tj * 128, tj * 128 + 128))
-            assert np.array_equal(codes[sl].cpu().numpy(), rc), t
-            assert _u32(scales[ti, tj:tj + 1])[0] == rs.view(np.uint32)[0], t
-            rd = oracle.dequantize(rc, fmt, PT, rs)
-            assert np.array_equal(_u32(deq[sl]).reshape(-1), rd.reshape(-1).view(np.uint32)), t
-            checked += 1
-    return checked
-
-
 def test_per_tensor_at_scale_full_compare(dev):
     """8192x8192 per-tensor: the whole tensor against the oracle (the input
     bits are the generator's, produced on the GPU and checked identical to
@@ -121,122 +85,6 @@ def test_per_tensor_at_scale_full_compare(dev):
         assert np.array_equal(codes.cpu().numpy(), rc), sp.name
         rd = oracle.dequantize(rc, sp.fmt, PT, rs)
         assert np.array_equal(_u32(deq), rd.reshape(-1).view(np.uint32)), sp.name
-
-
-def _check_row32_blocks(x_spec, codes, scales, deq, mx, fmt, rng, nsample):
-    """Sampled 1x32 blocks (FP32 scales, or MX E8M0 bytes when mx) against
-    the oracle on the block regenerated on the host."""
-    rows, cols = x_spec.rows, x_spec.cols
-    nb = rows * (cols // 32)
-    blocks = np.unique(np.concatenate([rng.integers(0, nb, nsample), [0, nb - 1]]))
-    for b in blocks:
-        r, j = divmod(int(b), cols // 32)
-        idx = torch.arange(r * cols + j * 32, r * cols + j * 32 + 32)
-        xb = x_spec.gen(idx).numpy().astype(np.uint16).reshape(1, 32)
-        sl = (slice(r, r + 1), slice(j * 32, (j + 1) * 32))
-        if mx:
-            rc, rs, _ = oracle.quantize_mx(xb, fmt)
-            rd = oracle.dequantize_mx(rc, fmt, rs)
-            assert int(scales[r, j].item()) == int(rs[0, 0]), b
-        else:
-            rc, rs, _ = oracle.quantize(xb, fmt, PT)
-            rd = oracle.dequantize(rc, fmt, PT, rs)
-            assert _u32(scales[r, j:j + 1])[0] == rs.view(np.uint32)[0], b
-        assert np.array_equal(codes[sl].cpu().numpy(), rc), b
-        assert np.array_equal(_u32(deq[sl]).reshape(-1), rd.reshape(-1).view(np.uint32)), b
-    return len(blocks)
-
-
-def test_row32_and_mx_blocks_at_full_size(dev):
-    """1x32 (FP32 scales) and MX 1x32 (E8M0) on the DeepSeek-V3 activation
-    shape and on the four 16384x32768 special-value tensors: sampled blocks
-    against the oracle, and the nonfinite flag over the whole tensor."""
-    rng = np.random.default_rng(66)
-    act = synth.deepseek_v3_blocks()[0]
-    checked = 0
-    for sp, fmts, nsample in [(act, (gs.FP8_E4M3,), 3000)] + \
-            [(s, (gs.FP8_E4M3, gs.FP8_E5M2), 400) for s in synth.special_values_4gib()]:
-        x = sp.full(dev)
-        expect_nf = None
-        for fmt in fmts:
-            for mx in (False, True):
-                nf = torch.zeros(1, dtype=torch.int32, device=dev)
-                if mx:
-                    codes, scales = gs.fp8_quantize_mx(x, fmt, nonfinite=nf)
-                    deq = gs.fp8_dequantize_mx(codes, fmt, scales)
-                else:
-                    codes, scales = gs.fp8_quantize(x, fmt, gs.FP8_BLOCK_1x32, nonfinite=nf)
-                    deq = gs.fp8_dequantize(codes, fmt, gs.FP8_BLOCK_1x32, scales)
-                torch.cuda.synchronize()
-                if expect_nf is None:
-                    expect_nf = int((~torch.isfinite(x.float())).any().item())
-                assert int(nf.item()) == expect_nf, (sp.name, fmt, mx)
-                checked += _check_row32_blocks(sp, codes, scales, deq, mx, fmt, rng, nsample)
-                del codes, scales, deq
-        del x
-        torch.cuda.empty_cache()
-    assert checked >= 2 * 2900 + 4 * 2 * 2 * 380
-
-
-def test_tensors_above_2_32_elements(dev):
-    """Maximum sizes: one FP16 gradient tensor of 2^32 + 6149 elements and
-    one 32896x131072 BF16 matrix (4.31e9 elements; the 1x128 and dequantize
-    grids are capped and stride).  Sampled outputs around the 2^31 and 2^32
-    element boundaries and at both ends against the oracle; an Inf past
-    2^32 sets the flag; the exact sum of squares against an FP64 sum."""
-    n = (1 << 32) + 3 * 2048 + 5
-    g = synth.GradSet(seed=7007, scale=2.0 ** 15, log2_lo=-18.0, log2_hi=12.0, steps=1)
-    g.tensors = [synth.GradSpec("big", n, 1)]
-    grad = g.full(0, dev)
-    out = torch.empty(n, dtype=torch.float32, device=dev)
-    S = torch.tensor([g.scale], dtype=torch.float32, device=dev)
-    f = torch.zeros(1, dtype=torch.int32, device=dev)
-    acc = torch.zeros(2, dtype=torch.int64, device=dev)
-    nsq = torch.zeros(1, dtype=torch.float64, device=dev)
-    gs.gs_unscale_check_sumsq([grad], [out], S, f, acc, nsq)
-    torch.cuda.synchronize()
-    assert int(f.item()) == 0
-    rng = np.random.default_rng(77)
-    edges = [np.arange(0, 4096), np.arange(n - 4096, n),
-             np.arange((1 << 31) - 2048, (1 << 31) + 2048), np.arange((1 << 32) - 2048, (1 << 32) + 2048)]
-    idx = np.unique(np.concatenate(edges + [rng.integers(0, n, 50000)]))
-    ti = torch.from_numpy(idx)
-    bits = g.gen(0, ti).numpy().astype(np.uint16)
-    ref, _ = oracle.unscale_check([bits], g.scale)
-    assert np.array_equal(_u32(out[ti.to(dev)]), ref[0].view(np.uint32))
-    tot = 0.0
-    for lo in range(0, n, 1 << 28):
-        tot += float((out[lo:lo + (1 << 28)].double() ** 2).sum().item())
-    assert abs(float(nsq.item()) - tot) <= 1e-12 * tot
-    pos = (1 << 32) + 7
-    grad[pos:pos + 1].fill_(float("inf"))
-    gs.gs_unscale_check([grad], [out], S, f)
-    torch.cuda.synchronize()
-    assert int(f.item()) == 1 and out[pos].item() == float("inf")
-    del grad, out
-    torch.cuda.empty_cache()
-
-    sp = synth.BitsSpec("big_random", 32896, 131072, 7007, 2, "random")
-    x = sp.full(dev)
-    for gran in (B1, B128):
-        codes, scales = gs.fp8_quantize(x, gs.FP8_E4M3, gran)
-        deq = gs.fp8_dequantize(codes, gs.FP8_E4M3, gran, scales)
-        torch.cuda.synchronize()
-        nb = _check_blocks(sp, codes, scales, deq, gran, gs.FP8_E4M3, rng, 600 if gran == B1 else 20)
-        assert nb >= (500 if gran == B1 else 15)
-        # the first and last block of the row that starts at element 2^32
-        if gran == B1:
-            r = (1 << 32) // sp.cols
-            for j in (0, sp.cols // 128 - 1):
-                idx = torch.arange(r * sp.cols + j * 128, r * sp.cols + j * 128 + 128)
-                xb = sp.gen(idx).numpy().astype(np.uint16).reshape(1, 128)
-                rc, rs, _ = oracle.quantize(xb, gs.FP8_E4M3, PT)
-                assert np.array_equal(codes[r, j * 128:(j + 1) * 128].cpu().numpy(), rc.reshape(-1))
-        del codes, scales, deq
-    codes, sc = gs.fp8_quantize_mx(x, gs.FP8_E5M2)
-    deq = gs.fp8_dequantize_mx(codes, gs.FP8_E5M2, sc)
-    torch.cuda.synchronize()
-    assert _check_row32_blocks(sp, codes, sc, deq, True, gs.FP8_E5M2, rng, 600) >= 500
 
 
 # ---------------------------------------------------------------- whole tensors
@@ -269,7 +117,7 @@ def _check_rows(xh, ch, sh, dh, fmt, gran, mode=gs.FP8_SCALE_FROM_AMAX, given=No
             rc, _, rnf = oracle.quantize(xh[sl], fmt, gran, mode, rs)
         else:
             rc, rs, rnf = oracle.quantize(xh[sl], fmt, gran)
-            got_s = sh[sl] if gran == B1 else sh[r0 // 128]
+            got_s = sh[r0 // 128] if gran == B128 else sh[sl]
             _bands_equal(got_s.reshape(-1), rs.reshape(-1).view(np.uint32), "scales", r0)
         _bands_equal(ch[sl], rc, "codes", r0)
         rd = oracle.dequantize(rc, fmt, gran if gran != PT else PT, rs)
@@ -421,3 +269,134 @@ def test_special_values_4gib_every_element(dev, name):
         flags.add(_check_rows(xh, ch, None, dh, fmt, PT, gs.FP8_SCALE_GIVEN, given=1.0))
         del ch, dh
     assert len(flags) == 1, flags                   # every mode saw the same inputs
+
+
+def _check_rows_mx(xh, ch, bh, dh, fmt):
+    """Every element of an MX quantize (E8M0 scale bytes bh, [rows, cols/32])
+    and its FP32 dequantize against the oracle, in bands of 128 rows; returns
+    the oracle's nonfinite flag."""
+    rows = xh.shape[0]
+
+    def band(r0):
+        sl = slice(r0, min(r0 + 128, rows))
+        rc, rb, rnf = oracle.quantize_mx(xh[sl], fmt)
+        _bands_equal(bh[sl], rb, "E8M0 scale bytes", r0)
+        _bands_equal(ch[sl], rc, "codes", r0)
+        _bands_equal(dh[sl], oracle.dequantize_mx(rc, fmt, rb).view(np.uint32),
+                     "dequantized values", r0)
+        return rnf
+
+    return max(_pmap(band, range(0, rows, 128)))
+
+
+@pytest.mark.timeout(900)
+def test_row32_and_mx_blocks_every_element(dev):
+    """1x32 blocks (FP32 scales) and MX 1x32 blocks (E8M0 bytes) on the
+    DeepSeek-V3 activation shape (E4M3) and on the four 16384x32768
+    special-value tensors (both formats): every code, scale and FP32
+    dequantized value against the oracle, and the nonfinite flag."""
+    act = synth.deepseek_v3_blocks()[0]
+    for sp, fmts in [(act, (gs.FP8_E4M3,))] + \
+            [(s, (gs.FP8_E4M3, gs.FP8_E5M2)) for s in synth.special_values_4gib()]:
+        x = sp.full(dev)
+        xh = _u16(x).reshape(sp.rows, sp.cols)
+        flags = set()
+        for fmt in fmts:
+            for mx in (False, True):
+                print("%s fmt %d %s" % (sp.name, fmt, "MX 1x32" if mx else "1x32"), flush=True)
+                nf = torch.zeros(1, dtype=torch.int32, device=dev)
+                if mx:
+                    codes, scales = gs.fp8_quantize_mx(x, fmt, nonfinite=nf)
+                    deq = gs.fp8_dequantize_mx(codes, fmt, scales)
+                else:
+                    codes, scales = gs.fp8_quantize(x, fmt, B32, nonfinite=nf)
+                    deq = gs.fp8_dequantize(codes, fmt, B32, scales)
+                torch.cuda.synchronize()
+                ch = codes.cpu().numpy()
+                sh = scales.cpu().numpy()
+                dh = deq.cpu().numpy().view(np.uint32)
+                del codes, scales, deq
+                if mx:
+                    rnf = _check_rows_mx(xh, ch, sh, dh, fmt)
+                else:
+                    rnf = _check_rows(xh, ch, sh.view(np.uint32), dh, fmt, B32)
+                assert int(nf.item()) == rnf, (sp.name, fmt, mx)
+                flags.add(rnf)
+                del ch, sh, dh
+        assert len(flags) == 1
+        del x
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_tensors_above_2_32_elements_every_element(dev):
+    """Maximum sizes, every element against the oracle: one FP16 gradient
+    tensor of 2^32 + 6149 elements through the unscale with the exact sum of
+    squares (the 128-bit total equal to the sum of the oracle's totals over
+    16M-element pieces, the norm equal to the oracle's for that total), and an
+    Inf past 2^32 setting the flag; one 32896x131072 BF16 matrix (4.31e9
+    elements; the 1x128, MX and dequantize grids are capped and stride)
+    quantized at 1x128 and 128x128 (E4M3) and MX 1x32 (E5M2), each with its
+    dequantize."""
+    n = (1 << 32) + 3 * 2048 + 5
+    g = synth.GradSet(seed=7007, scale=2.0 ** 15, log2_lo=-18.0, log2_hi=12.0, steps=1)
+    g.tensors = [synth.GradSpec("big", n, 1)]
+    grad = g.full(0, dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    S = torch.tensor([g.scale], dtype=torch.float32, device=dev)
+    f = torch.zeros(1, dtype=torch.int32, device=dev)
+    acc = torch.zeros(2, dtype=torch.int64, device=dev)
+    nsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    print("unscale + sum of squares, %d elements" % n, flush=True)
+    gs.gs_unscale_check_sumsq([grad], [out], S, f, acc, nsq)
+    torch.cuda.synchronize()
+    assert int(f.item()) == 0
+    xin, out_h = _u16(grad), _u32(out)
+    piece = 1 << 24
+
+    def check(lo):
+        ref, rf, racc, _ = oracle.unscale_check_sumsq([xin[lo:lo + piece]], g.scale)
+        _bands_equal(out_h[lo:lo + piece], ref[0].view(np.uint32), "unscaled outputs", lo)
+        return rf, racc[0] + (racc[1] << 64)
+
+    res = _pmap(check, range(0, n, piece))
+    assert max(r[0] for r in res) == 0
+    total = sum(r[1] for r in res)
+    got = [int(v) & ((1 << 64) - 1) for v in acc.cpu().tolist()]
+    assert got[0] + (got[1] << 64) == total
+    _, _, _, rnsq = oracle.unscale_check_sumsq([], g.scale, 0, (total & ((1 << 64) - 1), total >> 64))
+    assert float(nsq.item()) == rnsq
+    del out_h
+    pos = (1 << 32) + 7
+    grad[pos:pos + 1].fill_(float("inf"))
+    gs.gs_unscale_check([grad], [out], S, f)
+    torch.cuda.synchronize()
+    assert int(f.item()) == 1 and out[pos].item() == float("inf")
+    del grad, out, xin
+    torch.cuda.empty_cache()
+
+    sp = synth.BitsSpec("big_random", 32896, 131072, 7007, 2, "random")
+    x = sp.full(dev)
+    xh = _u16(x).reshape(sp.rows, sp.cols)
+    for gran in (B1, B128):
+        print("%dx%d gran %d" % (sp.rows, sp.cols, gran), flush=True)
+        nf = torch.zeros(1, dtype=torch.int32, device=dev)
+        codes, scales = gs.fp8_quantize(x, gs.FP8_E4M3, gran, nonfinite=nf)
+        deq = gs.fp8_dequantize(codes, gs.FP8_E4M3, gran, scales)
+        torch.cuda.synchronize()
+        ch, sh = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint32)
+        del codes, scales
+        dh = deq.cpu().numpy().view(np.uint32)
+        del deq
+        assert int(nf.item()) == _check_rows(xh, ch, sh, dh, gs.FP8_E4M3, gran)
+        del ch, sh, dh
+    print("%dx%d MX" % (sp.rows, sp.cols), flush=True)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    codes, sc = gs.fp8_quantize_mx(x, gs.FP8_E5M2, nonfinite=nf)
+    deq = gs.fp8_dequantize_mx(codes, gs.FP8_E5M2, sc)
+    torch.cuda.synchronize()
+    ch, bh = codes.cpu().numpy(), sc.cpu().numpy()
+    del codes, sc
+    dh = deq.cpu().numpy().view(np.uint32)
+    del deq
+    assert int(nf.item()) == _check_rows_mx(xh, ch, bh, dh, gs.FP8_E5M2)
