@@ -24,7 +24,9 @@
 // vector store, idempotent).  The update is one lane of one wave; nothing
 // ever comes back to the host.  The launch reserves unused LDS to hold the
 // kernel to 7 workgroups per CU, which measured faster than the 8 its
-// registers allow.
+// registers allow.  The sum-of-squares pass is left at those 8: each of its
+// workgroups also reduces its chunk's sums (two workgroup barriers), and on
+// the Llama-3-8B set it ran 2.3% faster uncapped (7.31 against 7.48 ms).
 #include "gs_internal.hpp"
 
 #include <atomic>
@@ -356,7 +358,8 @@ __global__ void update_scale_hysteresis_kernel(float *scale, int32_t *tracker, i
 // LDS per CU / 8 + 1 KiB).  At the 8 per CU its registers allow, MI355X
 // ran the Llama-3-8B gradient set 6-7% slower (7.7-7.9 ms against 7.28 ms):
 // more requests in flight than the memory system serves best.  Queried once
-// per device.
+// per device.  The sum-of-squares pass does not use it (see the top of the
+// file).
 constexpr int kMaxDevices = 64;
 std::atomic<unsigned> g_lds_reserve[kMaxDevices];
 
@@ -408,8 +411,8 @@ hipError_t launch_unscale_check_sumsq(const ChunkDesc *descs, int64_t nchunks, c
         const int64_t cap = GS_UNSCALE_GRID_CAP;
         const int64_t grid = nchunks < cap ? nchunks : cap;
         hipLaunchKernelGGL(unscale_check_kernel<true>, dim3((uint32_t)grid),
-                           dim3(kUnscaleThreads), unscale_lds_reserve(), stream, descs, nchunks,
-                           scale, found_inf, parts);
+                           dim3(kUnscaleThreads), 0, stream, descs, nchunks, scale, found_inf,
+                           parts);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         // about 8 or more partials per second-level thread
