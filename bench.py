@@ -204,7 +204,14 @@ class TimingEvents:
 
 
 CEIL_LIB = os.path.join(ROOT, "loss_scaling_fp8_amd", "libgsceil.so")
-CEIL_PATTERNS = {"read": 0, "write": 1, "expand_2to4": 2, "narrow_2to1": 3, "expand_1to4": 4}
+CEIL_PATTERNS = {"read": 0, "write": 1, "expand_2to4": 2, "narrow_2to1": 3, "expand_1to4": 4,
+                 "expand_1to2": 5}
+# bytes read and written by one pass of a pattern over n elements (read /
+# write: n bytes)
+CEIL_SRC_BYTES = {0: lambda n: n, 1: lambda n: 0, 2: lambda n: 2 * n, 3: lambda n: 2 * n,
+                  4: lambda n: n, 5: lambda n: n}
+CEIL_DST_BYTES = {0: lambda n: 0, 1: lambda n: n, 2: lambda n: 4 * n, 3: lambda n: n,
+                  4: lambda n: 4 * n, 5: lambda n: 2 * n}
 CEIL_POLICY = ("plain", "nt", "sc1nt")
 
 
@@ -234,8 +241,8 @@ def measure_ceilings(dev, specs, tev, reps=5):
     out = {}
     for name, pattern, n in specs:
         p = CEIL_PATTERNS[pattern]
-        src_bytes = {0: n, 1: 0, 2: 2 * n, 3: 2 * n, 4: n}[p]
-        dst_bytes = {0: 1024, 1: n, 2: 4 * n, 3: n, 4: 4 * n}[p]
+        src_bytes = CEIL_SRC_BYTES[p](n)
+        dst_bytes = CEIL_DST_BYTES[p](n) if p else 1024
         work = src_bytes + dst_bytes
         k = max(1, min(16, -(-(4 << 30) // work)))
         sets = [(torch.empty(max(src_bytes, 16), dtype=torch.uint8, device=dev),
@@ -302,6 +309,67 @@ def _time_launches(fn, reps, flush=None):
     return float(np.median(ts)), float(np.min(ts))
 
 
+def _ceil_lib():
+    import ctypes
+    L = ctypes.CDLL(CEIL_LIB)
+    L.gsc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_void_p]
+    L.gsc_stream.restype = ctypes.c_int
+    return L
+
+
+def _gsc_call(L, a):
+    rc = L.gsc_stream(*a)
+    if rc != 0:
+        raise RuntimeError("gsc_stream%r returned %d" % (a[:1] + a[3:9], rc))
+
+
+def _cold_best(L, p, src, dst, n, flush, reps, policies=(0, 1, 2)):
+    """Best median (ms, args) over the variants of single cold launches of
+    pattern p over n elements: unroll 1/2/4, both unit layouts, plain or
+    non-temporal loads, the given store policies, no cap or 6 workgroups per
+    CU."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for unroll in (1, 2, 4):
+        for layout in (0, 1):
+            for ntl in (0, 1):
+                for policy in ((0,) if p == 0 else policies):
+                    for occ in (0, 6):
+                        a = (p, src.data_ptr(), dst.data_ptr(), n, unroll, layout, ntl, policy,
+                             occ, stream)
+                        _gsc_call(L, a)
+                        ms, _ = _time_launches(lambda: _gsc_call(L, a), reps, flush)
+                        if best is None or ms < best[0]:
+                            best = (ms, a)
+    return best
+
+
+def cold_ceiling(dev, pattern, n, flush, policies=(0, 1, 2), reps=20):
+    """The least time one cold launch of `pattern` over n elements takes on
+    this GPU (milliseconds by HIP events), with its bytes moved: the best of
+    the streaming kernel's variants with the given store policies, each timed
+    after flush().  A cold launch with plain (write-back) stores can end
+    with part of its output still in the caches, so a write-heavy kernel is
+    compared with the ceiling of its own store class."""
+    import torch
+    L = _ceil_lib()
+    p = CEIL_PATTERNS[pattern]
+    src = torch.zeros(max(CEIL_SRC_BYTES[p](n), 16), dtype=torch.uint8, device=dev)
+    dst = torch.empty(max(CEIL_DST_BYTES[p](n), 1024), dtype=torch.uint8, device=dev)
+    ms, a = _cold_best(L, p, src, dst, n, flush, reps, policies)
+    del src, dst
+    unroll, layout, ntl, policy, occ = a[4:9]
+    return {"ms": round(ms, 4), "bytes": CEIL_SRC_BYTES[p](n) + CEIL_DST_BYTES[p](n),
+            "pattern": pattern,
+            "variant": "unroll %d (%s), %s loads, %s stores, %s" % (
+                unroll, "lane-contiguous units" if layout else "wave-contiguous units",
+                "non-temporal" if ntl else "plain", CEIL_POLICY[policy],
+                "no occupancy cap" if occ == 0 else "%d workgroups per CU" % occ)}
+
+
 def cold_two_pass_ceiling(dev, n, flush, reps=20):
     """The least a two-pass per-tensor quantize of n BF16 elements can take on
     this GPU, from the streaming kernels: the best variant of a cold read of
@@ -309,39 +377,16 @@ def cold_two_pass_ceiling(dev, n, flush, reps=20):
     same buffer, then the two launched back to back after a flush (the
     amax-then-cast sequence, with the second read finding what the first
     left in the caches).  Milliseconds by HIP events, medians of reps."""
-    import ctypes
     import torch
-    L = ctypes.CDLL(CEIL_LIB)
-    L.gsc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                             ctypes.c_void_p]
-    L.gsc_stream.restype = ctypes.c_int
-    stream = torch.cuda.current_stream().cuda_stream
+    L = _ceil_lib()
     src = torch.zeros(2 * n, dtype=torch.uint8, device=dev)
     dst = torch.empty(n, dtype=torch.uint8, device=dev)
     sink = torch.empty(1024, dtype=torch.uint8, device=dev)
-
-    def call(a):
-        rc = L.gsc_stream(*a)
-        if rc != 0:
-            raise RuntimeError("gsc_stream%r returned %d" % (a[:1] + a[3:9], rc))
-
-    best = {}
-    for p, nn, d, policies in ((0, 2 * n, sink, (0,)), (3, n, dst, (0, 1, 2))):
-        for unroll in (1, 2, 4):
-            for layout in (0, 1):
-                for ntl in (0, 1):
-                    for policy in policies:
-                        for occ in (0, 6):
-                            a = (p, src.data_ptr(), d.data_ptr(), nn, unroll, layout, ntl, policy,
-                                 occ, stream)
-                            call(a)
-                            ms, _ = _time_launches(lambda: call(a), reps, flush)
-                            if p not in best or ms < best[p][0]:
-                                best[p] = (ms, a)
-    seq, _ = _time_launches(lambda: (call(best[0][1]), call(best[3][1])), reps, flush)
+    rd = _cold_best(L, 0, src, sink, 2 * n, flush, reps)
+    nw = _cold_best(L, 3, src, dst, n, flush, reps)
+    seq, _ = _time_launches(lambda: (_gsc_call(L, rd[1]), _gsc_call(L, nw[1])), reps, flush)
     del src, dst, sink
-    return {"read_ms": round(best[0][0], 4), "narrow_2to1_ms": round(best[3][0], 4),
+    return {"read_ms": round(rd[0], 4), "narrow_2to1_ms": round(nw[0], 4),
             "read_then_narrow_ms": round(seq, 4),
             "note": "streaming kernels on the same sizes, cold; best of 24 read and 72 "
                     "2 B -> 1 B variants, then the best two back to back"}
@@ -779,6 +824,24 @@ def main():
         dw_bf = torch.empty((wgt.rows, wgt.cols), dtype=torch.bfloat16, device=dev)
         act_wl = "%dx%d bf16 E4M3, cold (clean) infinity cache" % (act.rows, act.cols)
         wgt_wl = "%dx%d bf16 E4M3 128x128, cold (clean) infinity cache" % (wgt.rows, wgt.cols)
+        # the same patterns streamed cold by the ceiling kernels, one launch
+        # after the same flush: what a single cold launch of that size can reach
+        cold = {}
+        if not args.pmc_safe and not args.no_ceilings:
+            # the quantizers store codes with plain stores, the dequantizers
+            # their outputs with non-temporal ones: each is compared with the
+            # streaming kernel restricted to the same store class
+            for cname, pat, ne, pol in (("narrow_2to1_act", "narrow_2to1", n_a, (0,)),
+                                        ("expand_1to4_act", "expand_1to4", n_a, (1, 2)),
+                                        ("expand_1to2_act", "expand_1to2", n_a, (1, 2)),
+                                        ("expand_1to2_wgt", "expand_1to2", n_w, (1, 2))):
+                cold[cname] = cold_ceiling(dev, pat, ne, flush, pol)
+            ext["cold_ceilings"] = cold
+        ext_ceil = {"quant_1x128_cold": "narrow_2to1_act", "quant_1x32": "narrow_2to1_act",
+                    "quant_mx_e8m0": "narrow_2to1_act", "dequant_1x128_cold": "expand_1to4_act",
+                    "dequant_1x32": "expand_1to4_act", "dequant_mx_e8m0": "expand_1to4_act",
+                    "dequant_1x128_bf16": "expand_1to2_act",
+                    "dequant_128x128_bf16": "expand_1to2_wgt"}
         for name, fn, nbytes, wl in (
                 ("quant_1x128_cold", lambda: gs.fp8_quantize(xa, act.fmt, act.gran, 0, ca, sa),
                  n_a * 3 + nb128 * 4, act_wl),
@@ -803,6 +866,11 @@ def main():
             gbps = nbytes / (ms_k * 1e-3) / 1e9
             ext[name] = {"ms": round(ms_k, 4), "bytes": nbytes, "GBps": round(gbps, 1),
                          "frac_of_peak": round(gbps / PEAK_GBPS, 4), "workload": wl}
+            c = cold.get(ext_ceil.get(name))
+            if c:
+                cg = c["bytes"] / (c["ms"] * 1e-3) / 1e9
+                ext[name]["cold_ceiling"] = ext_ceil[name]
+                ext[name]["frac_of_cold_ceiling"] = round(gbps / cg, 4)
         del junk, junk_rd, s32, smx, da_bf, dw_bf
 
     src_hash = kernel_source_hash(["unscale.hip", "gs_internal.hpp"])

@@ -17,6 +17,8 @@
 //                      quantizers' pattern
 //   4 1 B -> 4 B       4 bytes -> 4 FP32 per unit (4-byte load, 16-byte
 //                      store): the FP32 dequantizers' pattern
+//   5 1 B -> 2 B       8 bytes -> 8 16-bit values per unit (8-byte load,
+//                      16-byte store): the BF16 dequantizers' pattern
 // Variants: U in {1, 2, 4, 8}; layout 0 or 1; plain or non-temporal loads; store policy 0
 // plain, 1 non-temporal, 2 a buffer store with the device-scope
 // non-temporal policy (sc1 nt); and an occupancy cap of k workgroups per CU
@@ -125,6 +127,25 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
                                  hi_bytes(b[u].x, b[u].y), hi_bytes(b[u].z, b[u].w)};
                 if (base + i < nunits) put16<POLICY>(d, uint32_t(i) * 16u, o);
             }
+        } else if constexpr (PATTERN == 5) {
+            const u32x2 *s = static_cast<const u32x2 *>(src) + base;
+            void *d = static_cast<u32x4 *>(dst) + base;
+            u32x2 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
+                v[u] = base + i < nunits ? get<NTL>(s + i) : u32x2{0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = LAYOUT == 0 ? u * kThreads + threadIdx.x : threadIdx.x * U + u;
+                // each byte becomes the high byte of a 16-bit value
+                const u32x4 o = {((v[u].x << 8) & 0xFF00u) | ((v[u].x << 16) & 0xFF000000u),
+                                 ((v[u].x >> 8) & 0xFF00u) | (v[u].x & 0xFF000000u),
+                                 ((v[u].y << 8) & 0xFF00u) | ((v[u].y << 16) & 0xFF000000u),
+                                 ((v[u].y >> 8) & 0xFF00u) | (v[u].y & 0xFF000000u)};
+                if (base + i < nunits) put16<POLICY>(d, uint32_t(i) * 16u, o);
+            }
         } else {
             const uint32_t *s = static_cast<const uint32_t *>(src) + base;
             void *d = static_cast<f32x4 *>(dst) + base;
@@ -147,7 +168,7 @@ void stream_kernel(const void *__restrict__ src, void *__restrict__ dst, int64_t
 }
 
 // elements per unit of each pattern (read/write: bytes per unit)
-constexpr int64_t kElemsPerUnit[5] = {16, 16, 4, 16, 4};
+constexpr int64_t kElemsPerUnit[6] = {16, 16, 4, 16, 4, 8};
 
 template <int PATTERN, int U, bool NTL, int LAYOUT>
 hipError_t launch_u(int policy, const void *src, void *dst, int64_t nunits, uint32_t *sink,
@@ -196,7 +217,7 @@ hipError_t launch_p(int unroll, bool ntl, int layout, int policy, const void *sr
 // true here).  Returns 0, -1 for bad arguments, or the HIP error code.
 extern "C" int gsc_stream(int pattern, const void *src, void *dst, int64_t n, int unroll,
                           int layout, int nt_loads, int policy, int wgs_per_cu, void *stream) {
-    if (pattern < 0 || pattern > 4 || n < 0 || policy < 0 || policy > 2 || wgs_per_cu < 0 ||
+    if (pattern < 0 || pattern > 5 || n < 0 || policy < 0 || policy > 2 || wgs_per_cu < 0 ||
         (nt_loads != 0 && nt_loads != 1) || (layout != 0 && layout != 1))
         return -1;
     if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return -1;
@@ -222,7 +243,8 @@ extern "C" int gsc_stream(int pattern, const void *src, void *dst, int64_t n, in
         case 1: e = launch_p<1>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
         case 2: e = launch_p<2>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
         case 3: e = launch_p<3>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
-        default: e = launch_p<4>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
+        case 4: e = launch_p<4>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
+        default: e = launch_p<5>(unroll, nt_loads == 1, layout, policy, src, dst, nunits, sink, lds, s); break;
     }
     return e == hipSuccess ? 0 : int(e);
 }
