@@ -48,3 +48,37 @@ def test_committed_counters_are_read_only_for_their_own_source():
     traffic = bench.pmc_traffic(stored[0])
     assert traffic is not None and traffic > 48181567488     # above the algorithmic bytes
     assert bench.pmc_traffic("0" * 16) is None
+
+
+def test_ceiling_patterns_agree_with_the_streaming_library():
+    """Every pattern bench.py names has its byte counts, and the streaming
+    library accepts exactly those pattern numbers: its argument checks
+    (pattern, unroll, layout, policy, whole units, 16-byte alignment) return
+    -1 before any HIP call, and an empty stream returns 0, so this runs
+    without a GPU."""
+    import ctypes
+    if not os.path.exists(bench.CEIL_LIB):
+        import pytest
+        pytest.skip("libgsceil.so is not built")
+    L = ctypes.CDLL(bench.CEIL_LIB)
+    L.gsc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_void_p]
+    L.gsc_stream.restype = ctypes.c_int
+    assert sorted(bench.CEIL_PATTERNS.values()) == list(range(6))
+    for p in bench.CEIL_PATTERNS.values():
+        assert p in bench.CEIL_SRC_BYTES and p in bench.CEIL_DST_BYTES
+        assert L.gsc_stream(p, None, None, 0, 1, 0, 0, 0, 0, None) == 0       # nothing to do
+    unit = {0: 16, 1: 16, 2: 4, 3: 16, 4: 4, 5: 8}
+    for p, u in unit.items():
+        assert L.gsc_stream(p, None, None, u + 1, 1, 0, 0, 0, 0, None) == -1  # not whole units
+        assert L.gsc_stream(p, 8, None, u, 1, 0, 0, 0, 0, None) == -1        # misaligned source
+    assert L.gsc_stream(6, None, None, 0, 1, 0, 0, 0, 0, None) == -1
+    assert L.gsc_stream(5, None, None, 8, 3, 0, 0, 0, 0, None) == -1          # unroll 3
+    assert L.gsc_stream(5, None, None, 8, 1, 2, 0, 0, 0, None) == -1          # layout 2
+    assert L.gsc_stream(5, None, None, 8, 1, 0, 0, 3, 0, None) == -1          # policy 3
+    # the byte counts of one pass over n elements
+    n = 1 << 20
+    moved = {p: bench.CEIL_SRC_BYTES[p](n) + bench.CEIL_DST_BYTES[p](n)
+             for p in bench.CEIL_PATTERNS.values()}
+    assert moved == {0: n, 1: n, 2: 6 * n, 3: 3 * n, 4: 5 * n, 5: 3 * n}
