@@ -11,7 +11,7 @@ Workloads (seeded, synthetic; see synth/):
     scale, so their outputs are compared with step 3's on the device; the
     flag and S / tracker / skips at every step;
   * DeepSeek-V3-shaped BF16 activations 16384x7168 (1x128) and weights
-    7168x18432 (128x128), E4M3: codes, scales, FP32 dequantize;
+    7168x18432 (128x128), E4M3: codes, scales, FP32 and BF16 dequantize;
   * 8192x8192 per-tensor E4M3 (0.1% x1000 outliers) and E5M2 (Laplace);
   * four 16384x32768 special-value tensors: every granularity, both
     formats, scales from the amax and given scales of 1, with dequantize;
@@ -96,14 +96,14 @@ def _bands_equal(got, ref, what, where):
             [hex(int(ref[tuple(b)])) for b in bad]))
 
 
-def _check_rows(xh, ch, sh, dh, fmt, gran, mode=gs.FP8_SCALE_FROM_AMAX, given=None):
+def _check_rows(xh, ch, sh, dh, fmt, gran, mode=gs.FP8_SCALE_FROM_AMAX, given=None, bh=None):
     """Every element of a quantize + dequantize against the oracle, in bands
     of 128 rows (whole blocks at every granularity).  xh: BF16 bits
     [rows, cols]; ch codes; sh scales as uint32 bits in the block layout
     ([rows, cols/128], [rows/128, cols/128], or [1]); dh dequantized FP32 as
-    uint32 bits.  Per-tensor bands cast with `given`, the scale the oracle
-    derived from the whole tensor (or the given scale).  Returns the
-    oracle's nonfinite flag."""
+    uint32 bits; bh, when given, the BF16-output dequantize as uint16 bits.
+    Per-tensor bands cast with `given`, the scale the oracle derived from the
+    whole tensor (or the given scale).  Returns the oracle's nonfinite flag."""
     rows = xh.shape[0]
 
     def band(r0):
@@ -122,6 +122,9 @@ def _check_rows(xh, ch, sh, dh, fmt, gran, mode=gs.FP8_SCALE_FROM_AMAX, given=No
         _bands_equal(ch[sl], rc, "codes", r0)
         rd = oracle.dequantize(rc, fmt, gran if gran != PT else PT, rs)
         _bands_equal(dh[sl], rd.view(np.uint32), "dequantized values", r0)
+        if bh is not None:
+            rb = oracle.dequantize_bf16(rc, fmt, gran, rs)
+            _bands_equal(bh[sl], rb.view(np.uint16), "BF16 dequantized values", r0)
         return rnf
 
     return max(_pmap(band, range(0, rows, 128)))
@@ -141,13 +144,15 @@ def test_deepseek_v3_block_shapes_every_element(dev):
         nf = torch.zeros(1, dtype=torch.int32, device=dev)
         codes, scales = gs.fp8_quantize(x, sp.fmt, sp.gran, nonfinite=nf)
         deq = gs.fp8_dequantize(codes, sp.fmt, sp.gran, scales)
+        deq_bf = gs.fp8_dequantize_bf16(codes, sp.fmt, sp.gran, scales)
         torch.cuda.synchronize()
         assert tuple(scales.shape) == gs.scale_shape(sp.rows, sp.cols, sp.gran)
         xh = _u16(x).reshape(sp.rows, sp.cols)
         ch = codes.cpu().numpy()
         sh = scales.cpu().numpy().view(np.uint32)
         dh = deq.cpu().numpy().view(np.uint32)
-        rnf = _check_rows(xh, ch, sh, dh, sp.fmt, sp.gran)
+        bh = _u16(deq_bf).reshape(sp.rows, sp.cols)
+        rnf = _check_rows(xh, ch, sh, dh, sp.fmt, sp.gran, bh=bh)
         assert int(nf.item()) == rnf == 0
 
 
