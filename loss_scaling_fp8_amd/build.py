@@ -62,6 +62,28 @@ def _link(objs: list[str], lib: str) -> None:
     os.replace(tmp, lib)
 
 
+def build_variant(lib: str, defines: list[str]) -> str:
+    """The library built with extra preprocessor definitions (for example the
+    tiny grid caps of a test build), linked to `lib`; objects go to a
+    directory of their own beside it."""
+    obj_dir = os.path.join(os.path.dirname(lib), "_obj_" + os.path.basename(lib))
+    os.makedirs(obj_dir, exist_ok=True)
+
+    def one(src: str) -> str:
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *CXXFLAGS, *defines, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+        return obj
+
+    srcs = sources()
+    with ThreadPoolExecutor(min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(one, srcs))
+    _link(objs, lib)
+    return lib
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link both shared libraries (always)."""
     os.makedirs(OBJ_DIR, exist_ok=True)

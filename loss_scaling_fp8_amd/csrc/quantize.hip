@@ -788,7 +788,12 @@ void dequant_tiles_kernel(const uint8_t *__restrict__ codes, int64_t n, int64_t 
     }
 }
 
-constexpr int64_t kMaxGrid = int64_t(1) << 20;
+// Largest grid of any launch here; past it the kernels stride.  A test build
+// sets a tiny cap, so that every grid-stride path runs at small sizes.
+#ifndef GS_MAX_GRID
+#define GS_MAX_GRID (1 << 20)
+#endif
+constexpr int64_t kMaxGrid = GS_MAX_GRID;
 
 // Dynamic LDS that caps a block quantizer at `wgs` workgroups per CU (0: no
 // cap), from the device's LDS per CU (queried once per device).
@@ -851,6 +856,7 @@ hipError_t quantize_typed(const IN *x, int64_t rows, int64_t cols, int gran, uin
         int64_t p = (n + unit - 1) / unit;
         if (p < 1) p = 1;
         if (p > (stream_big ? kPartialSlots : kFoldParts)) p = stream_big ? kPartialSlots : kFoldParts;
+        if (p > kMaxGrid) p = kMaxGrid;
         if (stream_big)
             hipLaunchKernelGGL((amax_partials_kernel<IN, true>), dim3((uint32_t)p), dim3(256), 0,
                                stream, x, n, partials, nonfinite);
@@ -885,6 +891,7 @@ hipError_t quantize_delayed_typed(const IN *x, int64_t rows, int64_t cols, float
     int64_t g = (n / 32 + 255) / 256;            // one 32-element piece per lane
     if (g < 1) g = 1;
     if (g > kPartialSlots) g = kPartialSlots;
+    if (g > kMaxGrid) g = kMaxGrid;
     hipLaunchKernelGGL((quant_tensor_kernel<FMT, true, IN, true>), dim3((uint32_t)g), dim3(256),
                        0, stream, x, n, codes, scale_state, nonfinite, partials);
     hipError_t e = hipGetLastError();
