@@ -94,3 +94,27 @@ def test_per_tensor_and_plain_unscale_strided(dev, capped):
     for t, (o, r) in enumerate(zip(outs, ref)):
         assert np.array_equal(random_cases._u32(o), r.view(np.uint32)), t
     assert int(found.item()) == rflag
+
+
+def test_per_tensor_streaming_path_strided(dev, capped):
+    """A tensor larger than the infinity cache (8192x12800 BF16, 210 MB)
+    takes the other per-tensor path: the streaming partial-max pass, the
+    one-workgroup finalize, then the cast; with the caps, 3 workgroups each
+    stride over all of it."""
+    rng = np.random.default_rng(37)
+    rows, cols = 8192, 12800
+    assert rows * cols * 2 > 192 << 20
+    xf = rng.standard_normal((rows, cols), dtype=np.float32)
+    xf.reshape(-1)[rng.integers(0, xf.size, 1000)] *= 1e4
+    xf.reshape(-1)[rng.integers(0, xf.size, 10)] = np.nan
+    xh = (xf.view(np.uint32) >> 16).astype(np.uint16)           # BF16 by truncation
+    del xf
+    x = random_cases._to_dev(xh, dev)
+    for fmt in (gs.FP8_E4M3, gs.FP8_E5M2):
+        nf = torch.zeros(1, dtype=torch.int32, device=dev)
+        codes, sc = gs.fp8_quantize(x, fmt, gs.FP8_PER_TENSOR, nonfinite=nf)
+        rc, rs, rnf = oracle.quantize(xh, fmt, gs.FP8_PER_TENSOR)
+        torch.cuda.synchronize()
+        assert random_cases._u32(sc)[0] == rs.view(np.uint32)[0], fmt
+        assert np.array_equal(codes.cpu().numpy(), rc), fmt
+        assert int(nf.item()) == rnf == 1, fmt
