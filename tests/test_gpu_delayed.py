@@ -87,3 +87,29 @@ def test_delayed_large_and_empty(dev):
         assert _u32(used)[0] == np.float32(rused).view(np.uint32)
         assert np.array_equal(_u32(hist), R.history.view(np.uint32))
         assert _u32(st)[0] == R.scale.view(np.uint32)[0]
+
+
+def test_delayed_longest_history(dev):
+    """The largest history the ABI accepts (1024 entries, one per lane of
+    the update workgroup), with the ring position already past the first
+    wrap, and one entry past the limit refused."""
+    hlen = 1024
+    rng = np.random.default_rng(1024)
+    R = oracle.DelayedState(hlen, init_scale=0.5)
+    R.pos[0] = 2 * hlen - 3                  # reduced modulo the length
+    st = torch.tensor([0.5], dtype=torch.float32, device=dev)
+    hist = torch.zeros(hlen, dtype=torch.float32, device=dev)
+    pos = torch.tensor([2 * hlen - 3], dtype=torch.int32, device=dev)
+    for t, xf in enumerate(_steps(rng, (96, 160), 11)):
+        x = torch.from_numpy(xf).to(dev)
+        codes, used = gs.fp8_quantize_delayed(x, gs.FP8_E4M3, st, hist, pos)
+        rc, rused, _ = oracle.quantize_delayed(xf, gs.FP8_E4M3, R)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), rc), (t, "codes")
+        assert _u32(used)[0] == np.float32(rused).view(np.uint32), (t, "scale used")
+        assert np.array_equal(_u32(hist), R.history.view(np.uint32)), (t, "history")
+        assert int(pos.item()) == int(R.pos[0]), (t, "pos")
+        assert _u32(st)[0] == R.scale.view(np.uint32)[0], (t, "next scale")
+    big = torch.zeros(hlen + 1, dtype=torch.float32, device=dev)
+    with pytest.raises(gs.GSError):
+        gs.fp8_quantize_delayed(x, gs.FP8_E4M3, st, big, pos)
