@@ -290,3 +290,77 @@ def test_fp32_midpoints_with_non_power_of_two_scales(fmt, dev):
                                          (PT, (512, 1024), (512, 1024))):
         x = _fp32_midpoint_matrix(rng, rows, cols, fmt, br, bc)
         _check(x, fmt, gran, gs.FP8_SCALE_FROM_AMAX, dev)
+
+
+def _degenerate_bf16(rng, rows, cols, block_rows, block_cols):
+    """BF16 bit patterns where every block (block_rows x block_cols) is one
+    degenerate kind: all +0, all -0, all NaN, all +-Inf, NaN and Inf mixed,
+    all BF16 subnormals (amax below the 1e-12 floor times MAX), one huge
+    finite value among zeros, one value among NaNs, or ordinary N(0,1)."""
+    bits = np.zeros((rows, cols), np.uint16)
+    kinds = 9
+    for bi, r0 in enumerate(range(0, rows, block_rows)):
+        for bj, c0 in enumerate(range(0, cols, block_cols)):
+            b = bits[r0:r0 + block_rows, c0:c0 + block_cols]
+            kind = (bi * 7 + bj) % kinds
+            if kind == 1:
+                b[:] = 0x8000
+            elif kind == 2:
+                b[:] = 0x7FC0 | rng.integers(0, 0x40, b.shape).astype(np.uint16)
+            elif kind == 3:
+                b[:] = np.where(rng.random(b.shape) < 0.5, 0x7F80, 0xFF80)
+            elif kind == 4:
+                b[:] = np.where(rng.random(b.shape) < 0.5, 0x7FC1, 0xFF80)
+            elif kind == 5:
+                b[:] = rng.integers(1, 0x80, b.shape).astype(np.uint16) | \
+                    (rng.integers(0, 2, b.shape).astype(np.uint16) << 15)
+            elif kind == 6:
+                b.reshape(-1)[int(rng.integers(0, b.size))] = 0x7F7F       # the largest BF16
+            elif kind == 7:
+                b[:] = 0xFFC0
+                b.reshape(-1)[int(rng.integers(0, b.size))] = 0x3F80       # 1.0 among NaNs
+            elif kind == 8:
+                x = rng.standard_normal(b.shape).astype(np.float32)
+                b[:] = (x.view(np.uint32) >> 16).astype(np.uint16)
+    return bits
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_blocks_every_granularity(fmt, dtype, dev):
+    """Blocks that are entirely zero, NaN, Inf, subnormal, or a lone value
+    among zeros or NaNs, laid out on each granularity's own block grid
+    (and, for per-tensor, whole matrices of each kind), against the oracle:
+    the finite-only amax, the 1e-12 floor, saturation, NaN codes and the
+    MX power-of-two scale on every degenerate case."""
+    rng = np.random.default_rng(4242 + fmt + 2 * (dtype == "f32"))
+
+    def conv(bits):
+        x = bits if dtype == "bf16" else (bits.astype(np.uint32) << 16).view(np.float32)
+        return np.ascontiguousarray(x)
+
+    rows, cols = 384, 640
+    for gran, (br, bc) in ((B1, (1, 128)), (B32, (1, 32)), (B128, (128, 128))):
+        _check(conv(_degenerate_bf16(rng, rows, cols, br, bc)), fmt, gran,
+               gs.FP8_SCALE_FROM_AMAX, dev)
+    xmx = conv(_degenerate_bf16(rng, 96, 320, 1, 32))
+    xt = torch.from_numpy(xmx.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" \
+        else torch.from_numpy(xmx)
+    x = xt.to(dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    codes, sc = gs.fp8_quantize_mx(x, fmt, nonfinite=nf)
+    deq = gs.fp8_dequantize_mx(codes, fmt, sc)
+    rc, rs, rnf = oracle.quantize_mx(xmx, fmt)
+    rd = oracle.dequantize_mx(rc, fmt, rs)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), rc), "MX codes"
+    assert np.array_equal(sc.cpu().numpy(), rs), "MX scale bytes"
+    assert np.array_equal(_u32(deq), rd.reshape(-1).view(np.uint32)), "MX dequantized values"
+    assert int(nf.item()) == rnf
+    # per-tensor: a whole matrix of each kind (a ragged 77 x 93 one)
+    for kind_rows in range(9):
+        bits = _degenerate_bf16(rng, 77, 93, 77, 93)
+        if kind_rows:
+            bits = _degenerate_bf16(np.random.default_rng(kind_rows), 77 * 9, 93, 77, 93)
+            bits = np.ascontiguousarray(bits[77 * kind_rows:77 * (kind_rows + 1)])
+        _check(conv(bits), fmt, PT, gs.FP8_SCALE_FROM_AMAX, dev)
