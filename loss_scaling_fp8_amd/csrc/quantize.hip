@@ -610,9 +610,10 @@ void delayed_update_kernel(const uint32_t *__restrict__ partials, int nparts,
     // window maximum with this step's amax in slot p (history values are
     // non-negative floats, so their bit patterns order like their values)
     const int32_t p = ((*pos % hlen) + hlen) % hlen;
+    const int32_t tid = int32_t(threadIdx.x);
     uint32_t h = 0;
-    if (threadIdx.x < hlen)
-        h = (threadIdx.x == p) ? amax_t : as_u32(history[threadIdx.x]);
+    if (tid < hlen)
+        h = (tid == p) ? amax_t : as_u32(history[tid]);
     h = wave_max(h);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = h;
