@@ -32,7 +32,7 @@ CXXFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wextra", "-Wno-unused-command-line-argument",
 ]
 
 
